@@ -1,0 +1,312 @@
+"""Benchmark of the DeltaLog decode path on one MI355X.
+
+One bench "step" is one merge cycle: C decode tokens for every head of the
+batch (C-1 appends and the fused decode + fold), i.e. one pass over every
+stage of the path.  The headline value is the amortised time per token
+(cycle time / C) of GDN at B=128, H=32, d=128, C=8 with bf16 q/k/v and an fp32
+state, inputs resident in HBM.
+
+Printed: ONE JSON line.  Besides the contract fields it carries
+  roofline      the dominant kernel (the append) against 8 TB/s HBM:
+                algorithmic bytes per launch / mean launch time from HIP
+                events recorded around every launch of the timed region
+  cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample
+  eager         this library's eager dense kernel on the same inputs
+Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--C c]
+                       [--cold] [--report PATH] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "amortized µs/token + achieved HBM GB/s, GDN B=128 H=32 d=128 C=8"
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "append_gdn_b128_h32_d128_c8_traffic.md")
+KERNEL_SOURCES = ["recurrent_state_updates_amd/csrc/step_kernel.h",
+                  "recurrent_state_updates_amd/csrc/launch.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(per_launch_bytes):
+    """HBM bytes per append launch from the committed rocprofv3 counter summary,
+    or None when there is none or the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    with open(TRAFFIC_PROFILE) as f:
+        text = f.read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40, help="timed merge cycles")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed merge cycles")
+    ap.add_argument("--workload", default="gdn_b128_h32_d128")
+    ap.add_argument("--C", type=int, default=8, help="log capacity = merge interval")
+    ap.add_argument("--B", type=int, default=None, help="override the batch (sweep)")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each launch after flushing the 256 MB Infinity Cache")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-eager", action="store_true", help="skip the eager GPU kernel")
+    ap.add_argument("--cpu-tokens", type=int, default=24, help="tokens in the CPU-baseline sample")
+    ap.add_argument("--report", default=None, help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the decode path needs no exchange between GPUs "
+              "(heads are independent), so there is no multi-GPU run to time. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import recurrent_state_updates_amd as dl
+    import workloads
+    from recurrent_state_updates_amd import traffic
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dl.load_library()
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS[args.workload]
+    Bsz = args.B or w.B
+    C = args.C
+    print(f"# generating {w.name} B={Bsz} T={w.T}", file=sys.stderr, flush=True)
+    x = workloads.generate_workload(w, B=Bsz)
+    d = {k: (None if v is None else v.to(dev)) for k, v in x.items()}
+    T, H, D = w.T, w.H, w.d
+    sh = traffic.Shape(w.op, Bsz, H, D, 2 if w.in_dtype == "bf16" else 4)
+    outs = torch.empty((T, Bsz, H, D), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    base = d["S0"].clone()
+    st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
+    tok_args = [st.step_args(d["q"][t], d["k"][t], d["v"][t],
+                             None if d["beta"] is None else d["beta"][t], d["decay"][t], d["bonus"],
+                             outs[t]) for t in range(T)]
+    lib = dl.load_library()
+    step_fn = lib.dl_decode_step
+    handle = st.handle
+    import ctypes
+    arg_refs = [ctypes.byref(a) for a in tok_args]
+
+    def run_cycles(ncyc, tok0, events=None):
+        tok = tok0
+        for _ in range(ncyc):
+            for i in range(C):
+                if events is not None:
+                    events[0][i].record(stream)
+                rc = step_fn(handle, arg_refs[tok % T], sptr)
+                if events is not None:
+                    events[1][i].record(stream)
+                if rc != 0:
+                    raise dl.DeltaLogError(rc, dl.dl_last_error())
+                tok += 1
+        return tok
+
+    # warm-up, then the timed region with an event pair around every launch
+    tok = run_cycles(args.warmup, 0)
+    assert st.log_length == 0
+    K = args.steps
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(C)] for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for c in range(K):
+        tok = run_cycles(1, tok, evs[c])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_cycle = wall * 1e3 / K
+    us_per_token = wall * 1e6 / (K * C)
+    lat = np.array([[evs[c][0][i].elapsed_time(evs[c][1][i]) * 1e3 for i in range(C)] for c in range(K)])
+    kern_per_cycle = lat.sum(axis=1)
+    us_tok_events = float(np.median(kern_per_cycle)) / C
+
+    # a clean timed region without events, for the launch-overhead check
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    tok = run_cycles(K, tok)
+    torch.cuda.synchronize()
+    us_per_token_noev = (time.perf_counter() - t1) * 1e6 / (K * C)
+
+    append_us = [float(np.mean(lat[:, L])) for L in range(C - 1)]
+    merge_us = float(np.mean(lat[:, C - 1]))
+    cyc_bytes = traffic.cycle_bytes(sh, C)
+    tok_bytes = cyc_bytes / C
+    if C > 1:
+        app_bytes = [traffic.append_bytes(sh, L) for L in range(C - 1)]
+        dom_bytes = float(np.mean(app_bytes))
+        dom_us = float(np.mean(append_us))
+        dom_name = "append"
+    else:
+        dom_bytes = float(traffic.merge_bytes(sh, 1))
+        dom_us = merge_us
+        dom_name = "decode_fold"
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    measured = measured_traffic(dom_bytes) if (w.name == "gdn_b128_h32_d128" and C == 8 and Bsz == 128) else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(us_per_token, 3),
+        "unit": "us/token",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_cycle, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": w.op, "B": Bsz, "H": H, "dk": D, "dv": D, "C": C,
+                   "in_dtype": w.in_dtype, "state_dtype": "f32", "tokens_per_step": C,
+                   "seed": w.seed},
+        "achieved_GBps": round(tok_bytes / (us_per_token * 1e-6) / 1e9, 1),
+        "model_MB_per_token": round(tok_bytes / 1e6, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": measured, "kernel": dom_name,
+                     "algorithmic_bytes_per_launch": int(dom_bytes),
+                     "mean_launch_us": round(dom_us, 3)},
+        "kernels_us": {"append_by_L": [round(a, 2) for a in append_us], "decode_fold": round(merge_us, 2),
+                       "cycle_median_events": round(float(np.median(kern_per_cycle)), 2)},
+        "us_per_token_kernel_events": round(us_tok_events, 3),
+        "us_per_token_without_events": round(us_per_token_noev, 3),
+    }
+    st.close()
+    del st
+
+    if not args.no_eager:
+        state = d["S0"].clone()
+        cfg = dl.make_config(w.op, w.in_dtype, Bsz, H, D, D, 1)
+        eargs = [ctypes.byref(dl.state.make_step_args(
+            w.op, w.in_dtype, Bsz, H, D, D, dev, d["q"][t], d["k"][t], d["v"][t],
+            None if d["beta"] is None else d["beta"][t], d["decay"][t], d["bonus"], outs[t]))
+            for t in range(T)]
+        efn = lib.dl_eager_step
+        cref = ctypes.byref(cfg)
+        sp = state.data_ptr()
+        for t in range(args.warmup * C):
+            efn(cref, sp, eargs[t % T], sptr)
+        ne = K * C
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ne)] for _ in range(2)]
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for t in range(ne):
+            ev[0][t].record(stream)
+            rc = efn(cref, sp, eargs[t % T], sptr)
+            ev[1][t].record(stream)
+            if rc != 0:
+                raise dl.DeltaLogError(rc, dl.dl_last_error())
+        torch.cuda.synchronize()
+        e_wall_us = (time.perf_counter() - t2) * 1e6 / ne
+        e_lat = [ev[0][t].elapsed_time(ev[1][t]) * 1e3 for t in range(ne)]
+        e_us = float(np.mean(e_lat))
+        eb = traffic.eager_bytes(sh)
+        result["eager"] = {"us_per_token": round(e_wall_us, 3), "mean_launch_us": round(e_us, 3),
+                           "achieved_GBps": round(eb / (e_us * 1e-6) / 1e9, 1),
+                           "model_MB_per_token": round(eb / 1e6, 2)}
+        result["speedup_vs_eager"] = round(e_wall_us / us_per_token, 3)
+
+    if args.cold:
+        result["cold"] = cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(x, w, Bsz, args.cpu_tokens)
+
+    line = json.dumps(result)
+    print(line, flush=True)
+    if args.report:
+        with open(args.report, "a") as f:
+            f.write(line + "\n")
+
+
+def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs):
+    """Per-launch event times with a 512 MB write between launches (flushes the MALL)."""
+    import numpy as np
+    import torch
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    base = d["S0"].clone()
+    st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
+    ncyc = 6
+    lat = np.zeros((ncyc, C))
+    tok = 0
+    for c in range(ncyc):
+        for i in range(C):
+            flush.fill_(float(c * C + i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t = tok % w.T
+            e0.record(stream)
+            st.step(d["q"][t], d["k"][t], d["v"][t], None if d["beta"] is None else d["beta"][t],
+                    d["decay"][t], d["bonus"], outs[t])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            lat[c, i] = e0.elapsed_time(e1) * 1e3
+            tok += 1
+    st.close()
+    per_tok = float(np.median(lat.sum(axis=1))) / C
+    return {"us_per_token": round(per_tok, 3),
+            "achieved_GBps": round(traffic.per_token_bytes(sh, C) / (per_tok * 1e-6) / 1e9, 1),
+            "append_by_L": [round(float(np.median(lat[:, L])), 2) for L in range(C - 1)],
+            "decode_fold": round(float(np.median(lat[:, C - 1])), 2)}
+
+
+def cpu_baseline(x, w, Bsz, tokens):
+    """The fp64 oracle on the host cores: all heads of the batch, the first ``tokens`` tokens."""
+    import oracle
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    threads = max(1, min(16, ncpu))
+    T = min(tokens, w.T)
+    N = Bsz * w.H
+    D = w.d
+
+    def flat(t, width):
+        return t[:T].reshape(T, N, width).double().numpy()
+
+    beta = None if w.op == "rwkv6" else x["beta"][:T].reshape(T, N).double().numpy()
+    decay = x["decay"][:T].reshape(T, N).double().numpy() if w.op == "gdn" else flat(x["decay"], D)
+    bonus = None
+    if w.op == "rwkv6":
+        import numpy as np
+        bonus = x["bonus"].double().numpy()[np.arange(N) % w.H]
+    S0 = x["S0"].reshape(N, D, D).double().numpy()
+    q, k, v = flat(x["q"], D), flat(x["k"], D), flat(x["v"], D)
+    t0 = time.perf_counter()
+    oracle.eager_run(w.op, q, k, v, beta, decay, bonus, S0, nthreads=threads)
+    wall = time.perf_counter() - t0
+    return {"value": round(wall * 1e6 / T, 1), "unit": "us/token", "cores": threads, "kind": "oracle",
+            "sample": f"all {N} heads of {w.name} (B={Bsz}), first {T} tokens, fp64, "
+                      f"{threads} threads; wall {wall:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

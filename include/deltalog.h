@@ -1,0 +1,161 @@
+/*
+ * deltalog.h -- C ABI of the DeltaLog recurrent-state decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method.  "DeltaLog: Deferred Materialization of Recurrent States for Linear
+ * Attention Decoding" (Lin, Sun, Sun).  Each attention head of a linear-
+ * attention layer keeps a dense recurrent state of shape [dk, dv]; eager
+ * decoding rewrites the whole [B, H, dk, dv] tensor after every token
+ * although a token only contributes O(dk + dv) numbers (gist.science summary,
+ * section "Problema").  DeltaLog keeps instead a dense base state plus a
+ * bounded log of compact update factors and their log-decay metadata
+ * (section "Meccanismo Core: Base + Log"); it appends to the log while its
+ * length L is below the capacity C and folds the log into the base when L
+ * reaches C (signal-papers summary, caption of Fig. 4), so the logical state
+ * always equals the eager one (DeltaLog abstract).  Operators: GDN, KDA and
+ * RWKV6 (gist.science summary, section "Operatori").
+ *
+ * Logical state after L logged tokens (exact algebra, per head):
+ *     S = diag(e^{g_L}) Sbar + sum_{i<L} diag(e^{g_L - g_i}) k_i x_i^T
+ * with g_i the cumulative log-decay since the last fold, k_i the token's key
+ * and x_i its value-side factor: u_i = beta_i (v_i - (decayed state)^T k_i)
+ * for the delta rules (GDN, KDA), v_i for RWKV6.
+ *
+ * Conventions for every entry point:
+ *  - Device pointers are HIP device (or managed) memory owned by the caller.
+ *    The library never allocates, frees or synchronises device memory; it
+ *    enqueues kernels on the caller's stream and returns.  Inputs may be
+ *    reused or freed once the stream has passed the call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Every device pointer must be 16-byte aligned.  Buffers named as outputs
+ *    must not overlap inputs unless stated.
+ *  - Return values are dl_status codes: DL_OK (0) or a negative error.  On an
+ *    error nothing was enqueued and the handle is unchanged;
+ *    dl_last_error() then returns a message naming the argument at fault.
+ *    Faults inside a kernel (e.g. a freed buffer) surface asynchronously at
+ *    the caller's next synchronisation, not through these codes.
+ *  - A handle is not thread-safe; distinct handles are independent.
+ *
+ * Tensor layouts (row-major, last index contiguous; N = B*H heads, head
+ * n = b*H + h):
+ *    state / base  [B, H, dk, dv] fp32
+ *    q (r), k      [B, H, dk]     input dtype (fp32 or bf16)
+ *    v             [B, H, dv]     input dtype
+ *    beta          [B, H]         fp32   (GDN, KDA)
+ *    decay         GDN: alpha [B, H]; KDA: a [B, H, dk]; RWKV6: w [B, H, dk];
+ *                  fp32, every value in (0, 1] (0 is undefined behaviour)
+ *    bonus         [H, dk]        fp32   (RWKV6 per-head bonus u)
+ *    out           [B, H, dv]     fp32
+ * Supported shapes: dk == dv in {32, 64, 128}; 1 <= C <= DL_MAX_CAPACITY.
+ */
+#ifndef DELTALOG_H
+#define DELTALOG_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DL_MAX_CAPACITY 32
+
+typedef enum { DL_GDN = 0, DL_KDA = 1, DL_RWKV6 = 2 } dl_op;
+typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
+
+typedef enum {
+    DL_OK = 0,
+    DL_ERR_ARG = -1,          /* null or misaligned pointer, bad enum value, aliasing */
+    DL_ERR_SHAPE = -2,        /* non-positive or overflowing sizes, C out of [1, 32] */
+    DL_ERR_UNSUPPORTED = -3,  /* valid but not built: dk != dv or dk not in {32,64,128} */
+    DL_ERR_HIP = -4,          /* the HIP runtime refused a launch */
+    DL_ERR_WORKSPACE = -5     /* workspace smaller than dl_workspace_bytes() */
+} dl_status;
+
+/* Shape of one layer's recurrent state.  op: dl_op; in_dtype: dl_dtype of
+ * q (or r), k and v; B slots of H heads; key width dk, value width dv; log
+ * capacity C (the merge interval: tokens per fold). */
+typedef struct {
+    int op;
+    int in_dtype;
+    int B, H, dk, dv;
+    int C;
+} dl_config;
+
+/* Inputs and output of one decode token for all B*H heads.  beta must be
+ * NULL for RWKV6 and non-NULL otherwise; bonus must be non-NULL for RWKV6
+ * and NULL otherwise. */
+typedef struct {
+    const void *q;      /* q_t (GDN, KDA) or r_t (RWKV6)  [B,H,dk] in_dtype */
+    const void *k;      /* k_t                            [B,H,dk] in_dtype */
+    const void *v;      /* v_t                            [B,H,dv] in_dtype */
+    const float *beta;  /* beta_t [B,H] */
+    const float *decay; /* alpha_t [B,H] (GDN) or a_t / w_t [B,H,dk] */
+    const float *bonus; /* RWKV6 bonus u [H,dk] */
+    float *out;         /* o_t [B,H,dv] fp32, written */
+} dl_step_args;
+
+typedef struct dl_state dl_state; /* opaque, host memory only */
+
+/* Bytes of device workspace holding the log of capacity C for cfg (value
+ * factors, key copies and cumulative log-decays; see dl_workspace_layout).
+ * Returns 0 for an invalid or unsupported cfg. */
+size_t dl_workspace_bytes(const dl_config *cfg);
+
+/* Byte offsets inside the workspace of its three arrays, for inspection:
+ *   offsets[0]: value factors X [N][C][dv]  fp32 (GDN, KDA: u_i) or in_dtype (RWKV6: v_i)
+ *   offsets[1]: key copies    K [N][C][dk]  in_dtype (exact copies of k_i)
+ *   offsets[2]: log-decays    G [N][C] (GDN) or [N][C][dk] fp32, cumulative
+ *               base-2 log of the decay since the last fold, through token i
+ * Entry i of head n is valid for i < dl_log_length().  Returns DL_OK or an
+ * error for an invalid cfg or a NULL offsets. */
+dl_status dl_workspace_layout(const dl_config *cfg, size_t offsets[3]);
+
+/* Create a handle over a caller-owned base state and workspace.
+ *   base       [B,H,dk,dv] fp32 device memory holding the current dense state
+ *              (the initial state, or a state saved after a fold: resume)
+ *   workspace  device memory of at least dl_workspace_bytes(cfg) bytes
+ * The log starts empty (L = 0); no device work is done.  *out receives the
+ * handle (NULL on error).  The buffers must outlive the handle. */
+dl_status dl_state_init(dl_state **out, const dl_config *cfg, float *base,
+                        void *workspace, size_t workspace_bytes);
+
+/* Decode one token for every head (the append step; the signal-papers
+ * summary, Fig. 4, and gist.science "Fase di Append" / "Fase di Merge").
+ * Writes out = o_t.  If L + 1 < C it appends the token's compact factors
+ * and leaves the base untouched (L becomes L + 1).  If L + 1 == C the same
+ * launch also folds all C factors into the base with one read and one write
+ * of the base (L becomes 0).  With C == 1 every step is the eager update. */
+dl_status dl_decode_step(dl_state *h, const dl_step_args *args, void *stream);
+
+/* Fold the current log into the base now (an early merge), L becomes 0.
+ * Output-neutral: later outputs are unchanged.  A no-op when L == 0. */
+dl_status dl_merge(dl_state *h, void *stream);
+
+/* Write the logical dense state [B,H,dk,dv] fp32 into dst without changing
+ * the handle, the base or the log.  dst must not be the base. */
+dl_status dl_materialize(const dl_state *h, float *dst, void *stream);
+
+/* Current log length L in [0, C), or -1 for a NULL handle. */
+int dl_log_length(const dl_state *h);
+
+/* The eager dense update for comparison (gist.science "Problema"): reads
+ * the [B,H,dk,dv] fp32 state, writes out = o_t and the updated state in
+ * place.  Uses only cfg's op, in_dtype, B, H, dk, dv (C is ignored). */
+dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *args,
+                        void *stream);
+
+/* Release a handle (NULL is allowed).  Device buffers are not touched. */
+void dl_state_destroy(dl_state *h);
+
+/* Static description of a status code; never NULL. */
+const char *dl_status_string(int status);
+
+/* Message describing the last error returned on the calling thread
+ * ("" if none).  Valid until the thread's next call into the library. */
+const char *dl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTALOG_H */

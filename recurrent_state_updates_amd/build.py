@@ -1,0 +1,66 @@
+"""Build ``libdeltalog.so`` (HIP kernels + C ABI) for gfx950 with hipcc.
+
+Usage: ``python -m recurrent_state_updates_amd.build`` (or via
+``__graft_entry__.build()``).  Compiles every translation unit in parallel
+into ``_build/`` at the repository root and links the shared library next to
+this file.
+"""
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB = os.path.join(PKG, "libdeltalog.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+ARCH = "gfx950"
+
+SOURCES = ["deltalog.cpp", "kernels_gdn.hip", "kernels_kda.hip", "kernels_rwkv6.hip"]
+
+# Packed fp32 VALU ops are switched off for all device code; the host pass
+# prints that it does not know the feature, which is harmless.
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-I", os.path.join(ROOT, "include")]
+
+
+def _hipcc():
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; the HIP toolchain is required to build libdeltalog.so")
+    return path
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    lines = [ln for ln in res.stdout.splitlines() if "packed-fp32-ops' is not a recognized" not in ln]
+    if res.returncode != 0:
+        raise RuntimeError(f"command failed ({res.returncode}): {' '.join(cmd)}\n" + "\n".join(lines))
+    if verbose and lines:
+        print("\n".join(lines), flush=True)
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compile and link the library; returns its path."""
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([hipcc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

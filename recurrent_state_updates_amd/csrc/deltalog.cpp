@@ -1,0 +1,271 @@
+// deltalog.cpp -- the C ABI declared in include/deltalog.h: argument
+// validation, the host-side log-length bookkeeping and kernel dispatch.
+//
+// The handle lives in host memory only.  The log length L is the same for
+// every slot and head (lockstep batch decode), so it is tracked here and
+// passed to each launch; the launch mode follows from (L, C): append while
+// L + 1 < C, and decode + fold when the token fills the log (the
+// signal-papers summary, caption of Fig. 4: append while L < C, materialise
+// when L = C).
+#include "../../include/deltalog.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <limits>
+#include <new>
+#include <string>
+
+#include "launch.h"
+
+struct dl_state {
+    dl_config cfg;
+    float *base;
+    void *logX;
+    void *logK;
+    float *logG;
+    int L;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dl_status fail(dl_status st, const std::string &msg) {
+    g_last_error = msg;
+    return st;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t in_size(int dtype) { return dtype == DL_BF16 ? 2 : 4; }
+
+// Validate a config; on success *heads receives B*H.
+dl_status check_config(const dl_config *cfg, size_t *heads) {
+    if (!cfg) return fail(DL_ERR_ARG, "cfg is NULL");
+    if (cfg->op < DL_GDN || cfg->op > DL_RWKV6) return fail(DL_ERR_ARG, "cfg->op is not a dl_op");
+    if (cfg->in_dtype != DL_F32 && cfg->in_dtype != DL_BF16)
+        return fail(DL_ERR_ARG, "cfg->in_dtype is not a dl_dtype");
+    if (cfg->B <= 0 || cfg->H <= 0 || cfg->dk <= 0 || cfg->dv <= 0)
+        return fail(DL_ERR_SHAPE, "B, H, dk and dv must be positive");
+    if (cfg->C < 1 || cfg->C > DL_MAX_CAPACITY) return fail(DL_ERR_SHAPE, "C must lie in [1, 32]");
+    if (cfg->dk != cfg->dv) return fail(DL_ERR_UNSUPPORTED, "only dk == dv is built");
+    if (cfg->dk != 32 && cfg->dk != 64 && cfg->dk != 128)
+        return fail(DL_ERR_UNSUPPORTED, "dk must be 32, 64 or 128");
+    const size_t n = (size_t)cfg->B * (size_t)cfg->H;
+    // grid.x is an int; the largest array is N * C * D * 4 bytes
+    if (n > (size_t)std::numeric_limits<int>::max() ||
+        n > std::numeric_limits<size_t>::max() / ((size_t)DL_MAX_CAPACITY * 128 * 128 * 4))
+        return fail(DL_ERR_SHAPE, "B * H is too large");
+    *heads = n;
+    return DL_OK;
+}
+
+struct Layout {
+    size_t x, k, g, total;
+};
+
+Layout layout_of(const dl_config *cfg, size_t heads) {
+    const size_t entries = heads * (size_t)cfg->C;
+    const size_t xs = cfg->op == DL_RWKV6 ? in_size(cfg->in_dtype) : 4;
+    const size_t gw = cfg->op == DL_GDN ? 1 : (size_t)cfg->dk;
+    Layout l;
+    l.x = 0;
+    l.k = round_up(entries * cfg->dv * xs, 256);
+    l.g = l.k + round_up(entries * cfg->dk * in_size(cfg->in_dtype), 256);
+    l.total = l.g + round_up(entries * gw * 4, 256);
+    return l;
+}
+
+dl_status check_args(const dl_config *cfg, const dl_step_args *a) {
+    if (!a) return fail(DL_ERR_ARG, "args is NULL");
+    if (!a->q || !a->k || !a->v || !a->decay || !a->out)
+        return fail(DL_ERR_ARG, "args->q, k, v, decay and out must be non-NULL");
+    if (cfg->op == DL_RWKV6) {
+        if (a->beta) return fail(DL_ERR_ARG, "args->beta must be NULL for RWKV6");
+        if (!a->bonus) return fail(DL_ERR_ARG, "args->bonus is required for RWKV6");
+    } else {
+        if (!a->beta) return fail(DL_ERR_ARG, "args->beta is required for GDN and KDA");
+        if (a->bonus) return fail(DL_ERR_ARG, "args->bonus must be NULL for GDN and KDA");
+    }
+    const void *ptrs[] = {a->q, a->k, a->v, a->beta, a->decay, a->bonus, a->out};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(DL_ERR_ARG, "every device pointer must be 16-byte aligned");
+    return DL_OK;
+}
+
+dl_status launch(const dl_config *cfg, int mode, const dlk::StepParams &p, void *stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int cmax = cfg->C <= 8 ? 8 : 32;
+    const int bf16 = cfg->in_dtype == DL_BF16;
+    hipError_t e;
+    switch (cfg->op) {
+        case DL_GDN: e = dlk::launch_gdn(bf16, cfg->dk, mode, cmax, p, s); break;
+        case DL_KDA: e = dlk::launch_kda(bf16, cfg->dk, mode, cmax, p, s); break;
+        default: e = dlk::launch_rwkv6(bf16, cfg->dk, mode, cmax, p, s); break;
+    }
+    if (e != hipSuccess)
+        return fail(DL_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return DL_OK;
+}
+
+dlk::StepParams params_of(const dl_config *cfg, size_t heads) {
+    dlk::StepParams p = {};
+    p.C = cfg->C;
+    p.H = cfg->H;
+    p.N = (int)heads;
+    return p;
+}
+
+void set_token(dlk::StepParams &p, const dl_step_args *a) {
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.beta = a->beta;
+    p.decay = a->decay;
+    p.bonus = a->bonus;
+    p.out = a->out;
+}
+
+void set_log(dlk::StepParams &p, const dl_state *h) {
+    p.base = h->base;
+    p.logX = h->logX;
+    p.logK = h->logK;
+    p.logG = h->logG;
+    p.L = h->L;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dl_workspace_bytes(const dl_config *cfg) {
+    size_t heads = 0;
+    if (check_config(cfg, &heads) != DL_OK) return 0;
+    return layout_of(cfg, heads).total;
+}
+
+dl_status dl_workspace_layout(const dl_config *cfg, size_t offsets[3]) {
+    size_t heads = 0;
+    dl_status st = check_config(cfg, &heads);
+    if (st != DL_OK) return st;
+    if (!offsets) return fail(DL_ERR_ARG, "offsets is NULL");
+    const Layout l = layout_of(cfg, heads);
+    offsets[0] = l.x;
+    offsets[1] = l.k;
+    offsets[2] = l.g;
+    return DL_OK;
+}
+
+dl_status dl_state_init(dl_state **out, const dl_config *cfg, float *base, void *workspace,
+                        size_t workspace_bytes) {
+    if (!out) return fail(DL_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    size_t heads = 0;
+    dl_status st = check_config(cfg, &heads);
+    if (st != DL_OK) return st;
+    if (!base || !workspace) return fail(DL_ERR_ARG, "base and workspace must be non-NULL");
+    if (!aligned16(base) || !aligned16(workspace))
+        return fail(DL_ERR_ARG, "base and workspace must be 16-byte aligned");
+    const Layout l = layout_of(cfg, heads);
+    if (workspace_bytes < l.total)
+        return fail(DL_ERR_WORKSPACE, "workspace is smaller than dl_workspace_bytes(cfg) = " +
+                                          std::to_string(l.total));
+    dl_state *h = new (std::nothrow) dl_state;
+    if (!h) return fail(DL_ERR_ARG, "out of host memory");
+    char *ws = static_cast<char *>(workspace);
+    h->cfg = *cfg;
+    h->base = base;
+    h->logX = ws + l.x;
+    h->logK = ws + l.k;
+    h->logG = reinterpret_cast<float *>(ws + l.g);
+    h->L = 0;
+    *out = h;
+    g_last_error.clear();
+    return DL_OK;
+}
+
+dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
+    if (!h) return fail(DL_ERR_ARG, "handle is NULL");
+    size_t heads = 0;
+    dl_status st = check_config(&h->cfg, &heads);
+    if (st != DL_OK) return st;
+    st = check_args(&h->cfg, a);
+    if (st != DL_OK) return st;
+    dlk::StepParams p = params_of(&h->cfg, heads);
+    set_log(p, h);
+    set_token(p, a);
+    p.dst = h->base;
+    const bool fold = h->L + 1 == h->cfg.C;
+    st = launch(&h->cfg, fold ? dlk::MODE_MERGE : dlk::MODE_APPEND, p, stream);
+    if (st != DL_OK) return st;
+    h->L = fold ? 0 : h->L + 1;
+    return DL_OK;
+}
+
+dl_status dl_merge(dl_state *h, void *stream) {
+    if (!h) return fail(DL_ERR_ARG, "handle is NULL");
+    if (h->L == 0) return DL_OK;
+    size_t heads = 0;
+    dl_status st = check_config(&h->cfg, &heads);
+    if (st != DL_OK) return st;
+    dlk::StepParams p = params_of(&h->cfg, heads);
+    set_log(p, h);
+    p.dst = h->base;
+    st = launch(&h->cfg, dlk::MODE_FOLD, p, stream);
+    if (st != DL_OK) return st;
+    h->L = 0;
+    return DL_OK;
+}
+
+dl_status dl_materialize(const dl_state *h, float *dst, void *stream) {
+    if (!h) return fail(DL_ERR_ARG, "handle is NULL");
+    if (!dst) return fail(DL_ERR_ARG, "dst is NULL");
+    if (!aligned16(dst)) return fail(DL_ERR_ARG, "dst must be 16-byte aligned");
+    if (dst == h->base) return fail(DL_ERR_ARG, "dst must not be the base (use dl_merge)");
+    size_t heads = 0;
+    dl_status st = check_config(&h->cfg, &heads);
+    if (st != DL_OK) return st;
+    dlk::StepParams p = params_of(&h->cfg, heads);
+    set_log(p, h);
+    p.dst = dst;
+    return launch(&h->cfg, dlk::MODE_FOLD, p, stream);
+}
+
+int dl_log_length(const dl_state *h) { return h ? h->L : -1; }
+
+dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *a, void *stream) {
+    size_t heads = 0;
+    dl_status st = check_config(cfg, &heads);
+    if (st != DL_OK) return st;
+    if (!state) return fail(DL_ERR_ARG, "state is NULL");
+    if (!aligned16(state)) return fail(DL_ERR_ARG, "state must be 16-byte aligned");
+    st = check_args(cfg, a);
+    if (st != DL_OK) return st;
+    dlk::StepParams p = params_of(cfg, heads);
+    set_token(p, a);
+    p.base = state;
+    p.dst = state;
+    return launch(cfg, dlk::MODE_EAGER, p, stream);
+}
+
+void dl_state_destroy(dl_state *h) { delete h; }
+
+const char *dl_status_string(int status) {
+    switch (status) {
+        case DL_OK: return "ok";
+        case DL_ERR_ARG: return "invalid argument";
+        case DL_ERR_SHAPE: return "invalid shape";
+        case DL_ERR_UNSUPPORTED: return "unsupported configuration";
+        case DL_ERR_HIP: return "HIP runtime error";
+        case DL_ERR_WORKSPACE: return "workspace too small";
+        default: return "unknown status";
+    }
+}
+
+const char *dl_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,10 @@
+// Kernel instantiations for the GDN operator (see step_kernel.h).
+#include "step_kernel.h"
+
+namespace dlk {
+
+hipError_t launch_gdn(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s) {
+    return launch_op<OP_GDN>(in_bf16, D, mode, cmax, p, s);
+}
+
+}  // namespace dlk

@@ -1,0 +1,98 @@
+"""Algorithmic HBM bytes of each decode-path launch (the traffic model).
+
+Eager decoding moves the whole [B,H,dk,dv] state twice per token although a
+token adds only O(dk + dv) numbers per head (gist.science summary, section
+"Problema").  DeltaLog replaces the dense write of M-1 out of every M tokens
+with compact appends and one amortised dense write (section "Modello di
+Traffico").  These functions count the bytes each launch must move at
+minimum -- every input, log entry and state element read or written once --
+which is what "achieved GB/s" divides by.
+
+Per head, D = dk = dv, s = input element size (4 fp32, 2 bf16):
+  base tile        4 D^2
+  token inputs     q|r, k, v: 3 D s; beta 4 (delta rules); decay 4 (GDN) or 4 D
+  output           4 D
+  log entry        X: 4 D (u, delta rules) or D s (v, RWKV6); K: D s; G: 4 or 4 D
+  RWKV6 bonus      4 D per attention head, read once per launch (H rows)
+An append at log length L reads the base, the token and L entries and writes
+one entry and the output; the fused fold (L = C-1) also writes the base and
+writes no entry; eager reads and writes the state.
+"""
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class Shape:
+    op: str
+    B: int
+    H: int
+    d: int
+    in_bytes: int  # 4 (fp32) or 2 (bf16)
+
+    @property
+    def heads(self):
+        return self.B * self.H
+
+    def base(self):
+        return 4 * self.d * self.d
+
+    def token_in(self):
+        d, s = self.d, self.in_bytes
+        b = 3 * d * s
+        if self.op != "rwkv6":
+            b += 4  # beta
+        b += 4 if self.op == "gdn" else 4 * d
+        return b
+
+    def out(self):
+        return 4 * self.d
+
+    def entry(self):
+        d, s = self.d, self.in_bytes
+        x = d * s if self.op == "rwkv6" else 4 * d
+        g = 4 if self.op == "gdn" else 4 * d
+        return x + d * s + g
+
+    def shared(self):
+        return 4 * self.d * self.H if self.op == "rwkv6" else 0
+
+
+def append_bytes(sh: Shape, L: int) -> int:
+    """An append at log length L (the token becomes entry L)."""
+    per = sh.base() + sh.token_in() + sh.out() + (L + 1) * sh.entry()
+    return sh.heads * per + sh.shared()
+
+
+def merge_bytes(sh: Shape, C: int) -> int:
+    """The token that fills the log (L = C-1) fused with the fold into the base."""
+    per = 2 * sh.base() + sh.token_in() + sh.out() + (C - 1) * sh.entry()
+    return sh.heads * per + sh.shared()
+
+
+def eager_bytes(sh: Shape) -> int:
+    per = 2 * sh.base() + sh.token_in() + sh.out()
+    return sh.heads * per + sh.shared()
+
+
+def fold_bytes(sh: Shape, L: int) -> int:
+    """A standalone fold (merge or materialise) of L entries."""
+    return sh.heads * (2 * sh.base() + L * sh.entry())
+
+
+def cycle_bytes(sh: Shape, C: int) -> int:
+    """One merge cycle of C tokens: C-1 appends and the fused fold."""
+    if C == 1:
+        return merge_bytes(sh, 1)
+    return sum(append_bytes(sh, L) for L in range(C - 1)) + merge_bytes(sh, C)
+
+
+def per_token_bytes(sh: Shape, C: int) -> float:
+    return cycle_bytes(sh, C) / C
+
+
+def cycle_flops(sh: Shape, C: int) -> int:
+    """Useful FLOPs of one cycle: the base mat-vecs (two for delta rules, one
+    for RWKV6) every token, plus the rank-C fold and row scaling once."""
+    mv = (4 if sh.op != "rwkv6" else 2) * sh.d * sh.d
+    fold = 2 * C * sh.d * sh.d + sh.d * sh.d
+    return sh.heads * (C * mv + fold)

@@ -1,0 +1,164 @@
+"""Host side of the C ABI, on the CPU: exports, sizing and argument validation.
+
+No call here reaches a kernel: every call either fails validation before any
+HIP call, or (``dl_state_init``, ``dl_merge`` at L = 0, ``dl_log_length``,
+``dl_state_destroy``) does no device work by design.  Device addresses are
+fake, aligned integers that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import recurrent_state_updates_amd as dl
+from recurrent_state_updates_amd import _binding as B
+from recurrent_state_updates_amd import build as dlbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deltalog.h")
+FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        dlbuild.build()
+    return B.load_library()
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dl_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 11, names
+    for name in names:
+        assert hasattr(lib, name), f"{name} is declared in deltalog.h but not exported"
+    for name in names:
+        assert hasattr(dl, name), f"the Python binding lacks {name}"
+
+
+def test_status_strings():
+    assert dl.dl_status_string(0) == "ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert dl.dl_status_string(code) not in ("", "unknown status")
+    assert dl.dl_status_string(-99) == "unknown status"
+
+
+def _round(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("op,dtype,d,C", [("gdn", "bf16", 128, 8), ("kda", "bf16", 128, 4),
+                                          ("rwkv6", "bf16", 64, 8), ("gdn", "f32", 32, 4),
+                                          ("rwkv6", "f32", 32, 32)])
+def test_workspace_size_and_layout(op, dtype, d, C):
+    Bsz, H = 3, 5
+    cfg = dl.make_config(op, dtype, Bsz, H, d, d, C)
+    n = Bsz * H * C
+    isz = 2 if dtype == "bf16" else 4
+    xsz = isz if op == "rwkv6" else 4
+    gw = 1 if op == "gdn" else d
+    x = _round(n * d * xsz)
+    k = _round(n * d * isz)
+    g = _round(n * gw * 4)
+    assert dl.dl_workspace_bytes(cfg) == x + k + g
+    assert dl.dl_workspace_layout(cfg) == (0, x, x + k)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=7), B.DL_ERR_ARG), (dict(in_dtype=5), B.DL_ERR_ARG),
+    (dict(B=0), B.DL_ERR_SHAPE), (dict(H=-1), B.DL_ERR_SHAPE),
+    (dict(C=0), B.DL_ERR_SHAPE), (dict(C=33), B.DL_ERR_SHAPE),
+    (dict(dk=128, dv=64), B.DL_ERR_UNSUPPORTED), (dict(dk=96, dv=96), B.DL_ERR_UNSUPPORTED),
+])
+def test_invalid_configs(kw, code):
+    base = dict(op=0, in_dtype=1, B=2, H=2, dk=64, dv=64, C=4)
+    base.update(kw)
+    cfg = B.Config(**base)
+    assert dl.dl_workspace_bytes(cfg) == 0
+    with pytest.raises(dl.DeltaLogError) as ei:
+        dl.dl_state_init(cfg, FAKE, FAKE, 1 << 30)
+    assert ei.value.status == code
+    assert dl.dl_last_error() != ""
+
+
+def test_state_init_validation_and_bookkeeping():
+    cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)
+    need = dl.dl_workspace_bytes(cfg)
+    with pytest.raises(dl.DeltaLogError) as ei:
+        dl.dl_state_init(cfg, 0, FAKE, need)
+    assert ei.value.status == B.DL_ERR_ARG
+    with pytest.raises(dl.DeltaLogError) as ei:
+        dl.dl_state_init(cfg, FAKE + 4, FAKE, need)
+    assert ei.value.status == B.DL_ERR_ARG
+    with pytest.raises(dl.DeltaLogError) as ei:
+        dl.dl_state_init(cfg, FAKE, FAKE, need - 1)
+    assert ei.value.status == B.DL_ERR_WORKSPACE
+    lib = B.load_library()
+    assert lib.dl_state_init(None, ctypes.byref(cfg), FAKE, FAKE, need) == B.DL_ERR_ARG
+    h = dl.dl_state_init(cfg, FAKE, FAKE, need)
+    try:
+        assert dl.dl_log_length(h) == 0
+        dl.dl_merge(h)  # L == 0: a no-op, nothing is launched
+        assert dl.dl_log_length(h) == 0
+        with pytest.raises(dl.DeltaLogError) as ei:
+            dl.dl_materialize(h, FAKE)  # dst is the base
+        assert ei.value.status == B.DL_ERR_ARG
+        with pytest.raises(dl.DeltaLogError):
+            dl.dl_materialize(h, 0)
+        with pytest.raises(dl.DeltaLogError):
+            dl.dl_materialize(h, FAKE + 0x1000 + 8)
+    finally:
+        dl.dl_state_destroy(h)
+    assert dl.dl_log_length(None) == -1
+    dl.dl_state_destroy(None)
+
+
+def _args(**over):
+    a = dict(q=FAKE, k=FAKE + 0x100, v=FAKE + 0x200, beta=FAKE + 0x300, decay=FAKE + 0x400,
+             bonus=0, out=FAKE + 0x500)
+    a.update(over)
+    return B.StepArgs(**a)
+
+
+@pytest.mark.parametrize("op,over", [
+    ("gdn", dict(q=0)), ("gdn", dict(out=0)), ("gdn", dict(decay=0)), ("gdn", dict(beta=0)),
+    ("gdn", dict(bonus=FAKE + 0x600)), ("kda", dict(beta=0)),
+    ("rwkv6", dict()),  # beta given, bonus missing
+    ("rwkv6", dict(beta=0)),  # bonus missing
+    ("gdn", dict(k=FAKE + 0x102)), ("gdn", dict(out=FAKE + 0x508)),
+])
+def test_decode_step_rejects_bad_args_without_state_change(op, over):
+    cfg = dl.make_config(op, "bf16", 2, 4, 64, 64, 4)
+    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    try:
+        with pytest.raises(dl.DeltaLogError) as ei:
+            dl.dl_decode_step(h, _args(**over))
+        assert ei.value.status == B.DL_ERR_ARG
+        assert dl.dl_log_length(h) == 0
+        with pytest.raises(dl.DeltaLogError):
+            dl.dl_eager_step(cfg, FAKE, _args(**over))
+    finally:
+        dl.dl_state_destroy(h)
+    lib = B.load_library()
+    assert lib.dl_decode_step(None, ctypes.byref(_args()), None) == B.DL_ERR_ARG
+
+
+def test_eager_step_rejects_bad_state():
+    cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 1)
+    with pytest.raises(dl.DeltaLogError):
+        dl.dl_eager_step(cfg, 0, _args())
+    with pytest.raises(dl.DeltaLogError):
+        dl.dl_eager_step(cfg, FAKE + 4, _args())
+
+
+def test_library_is_built_for_gfx950():
+    with open(B.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"gfx950" in blob

@@ -68,7 +68,7 @@ def parse():
                     help="also time each launch after flushing the 256 MB Infinity Cache")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-eager", action="store_true", help="skip the eager GPU kernel")
-    ap.add_argument("--cpu-tokens", type=int, default=24, help="tokens in the CPU-baseline sample")
+    ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the CPU-baseline sample")
     ap.add_argument("--report", default=None, help="also append the JSON line to this file")
     return ap.parse_args()
 

@@ -27,8 +27,9 @@
  *    enqueues kernels on the caller's stream and returns.  Inputs may be
  *    reused or freed once the stream has passed the call.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *  - Every device pointer must be 16-byte aligned.  Buffers named as outputs
- *    must not overlap inputs unless stated.
+ *  - State buffers (base, dst, state) and the workspace must be 16-byte
+ *    aligned; every other device pointer must be aligned to its element
+ *    size.  Buffers named as outputs must not overlap inputs unless stated.
  *  - Return values are dl_status codes: DL_OK (0) or a negative error.  On an
  *    error nothing was enqueued and the handle is unchanged;
  *    dl_last_error() then returns a message naming the argument at fault.

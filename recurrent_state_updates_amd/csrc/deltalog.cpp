@@ -91,9 +91,15 @@ dl_status check_args(const dl_config *cfg, const dl_step_args *a) {
         if (!a->beta) return fail(DL_ERR_ARG, "args->beta is required for GDN and KDA");
         if (a->bonus) return fail(DL_ERR_ARG, "args->bonus must be NULL for GDN and KDA");
     }
-    const void *ptrs[] = {a->q, a->k, a->v, a->beta, a->decay, a->bonus, a->out};
-    for (const void *p : ptrs)
-        if (p && !aligned16(p)) return fail(DL_ERR_ARG, "every device pointer must be 16-byte aligned");
+    const size_t es = in_size(cfg->in_dtype);
+    const void *in_ptrs[] = {a->q, a->k, a->v};
+    for (const void *p : in_ptrs)
+        if (reinterpret_cast<uintptr_t>(p) % es != 0)
+            return fail(DL_ERR_ARG, "q, k and v must be aligned to their element size");
+    const void *f32_ptrs[] = {a->beta, a->decay, a->bonus, a->out};
+    for (const void *p : f32_ptrs)
+        if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
+            return fail(DL_ERR_ARG, "beta, decay, bonus and out must be 4-byte aligned");
     return DL_OK;
 }
 

@@ -132,7 +132,7 @@ def _args(**over):
     ("gdn", dict(bonus=FAKE + 0x600)), ("kda", dict(beta=0)),
     ("rwkv6", dict()),  # beta given, bonus missing
     ("rwkv6", dict(beta=0)),  # bonus missing
-    ("gdn", dict(k=FAKE + 0x102)), ("gdn", dict(out=FAKE + 0x508)),
+    ("gdn", dict(k=FAKE + 0x101)), ("gdn", dict(out=FAKE + 0x502)), ("gdn", dict(beta=FAKE + 0x302)),
 ])
 def test_decode_step_rejects_bad_args_without_state_change(op, over):
     cfg = dl.make_config(op, "bf16", 2, 4, 64, 64, 4)

@@ -149,7 +149,7 @@ def test_early_merge_is_output_neutral(op):
     dev = gs.to_device(x, DEV)
     o_ref, s_ref, _ = gs.run_deltalog(dev, op, "bf16", C, state_steps=[T])
     lengths = []
-    o_m, s_m, st = gs.run_deltalog(dev, op, "bf16", C, state_steps=[T], merge_after={3, 5, 11, 12, 29},
+    o_m, s_m, st = gs.run_deltalog(dev, op, "bf16", C, state_steps=[T], merge_after={3, 5, 11, 12, 30},
                                    on_step=lambda t, s: lengths.append(s.log_length))
     assert max(gs.rel(o_m[t].cpu(), o_ref[t].cpu()) for t in range(T)) <= 1e-5
     assert gs.rel(s_m[T].numpy(), s_ref[T].numpy()) <= 1e-5

@@ -1,9 +1,10 @@
 // step_kernel.h -- the decode-step kernel family for gfx950.
 //
-// One workgroup owns one head's D x D fp32 state tile.  Its threads stream
-// the tile once from HBM with coalesced 16-byte loads (a row is D/4 lanes
-// wide), keep it in registers, and do everything else around that single
-// pass:
+// One workgroup owns a D x TV tile of one head's fp32 state: all D key rows
+// and TV of the D value columns (the pages' value-tile parallelism).  Its
+// threads stream the tile once from HBM with coalesced 16-byte loads (a tile
+// row is TV/4 lanes wide), keep it in registers, and do everything else
+// around that single pass:
 //
 //   APPEND  o_t from base + log replay, new factor appended (base read only)
 //   MERGE   the same token, then the rank-C fold of the whole log into the
@@ -12,13 +13,14 @@
 //   FOLD    base + log written to a destination (merge / materialise)
 //
 // The method (DeltaLog; gist.science summary, sections "Meccanismo Core" and
-// "Implementazione del Kernel"): the per-head key-side work -- the replay
-// coefficients of every log entry, computed once per head -- is done in the
-// workgroup prologue from LDS while the base loads are in flight; the
-// value-side log shard of the tile is staged in LDS next to it.  With one
-// workgroup per head every value column of the head lives in the workgroup,
-// so the key-side work is done exactly once per head, as the pages' staged
-// ReplayPrep/AppendDecode split intends, without a second launch.
+// "Implementazione del Kernel"): the state is split along the value width;
+// each work unit owns a base slice and its value-side log shard, and the
+// key-side factors and log-decay metadata are shared by the tiles.  The
+// pages run the key-side replay preparation as a separate stage once per
+// slot-head; here every workgroup recomputes it in its prologue, from LDS,
+// while its base loads are in flight -- a few hundred FLOPs per head against
+// a 32 KB stream, cheaper than a second launch -- and the two tiles of a head
+// run on the same XCD so the second reads the key-side log from L2.
 //
 // Algebra, per head, with cumulative base-2 log-decays g (reset at a fold):
 //   logical state   S_L = diag(2^{g_L}) Sbar + sum_{i<L} diag(2^{g_L-g_i}) k_i x_i^T
@@ -50,25 +52,42 @@ __device__ __forceinline__ float to_f32(bf16_bits b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Thread geometry of one workgroup over one head's D x D tile.
-template <int D, int NT>
+// Thread geometry of one workgroup over a D x TV tile (all D key rows, TV of
+// the D value columns) of one head's state.
+template <int D, int TV, int NT>
 struct Geom {
-    static constexpr int LPR = D / 4;            // lanes per state row (one float4 each)
+    static constexpr int NTILE = D / TV;         // value tiles per head
+    static constexpr int LPR = TV / 4;           // lanes per tile row (one float4 each)
     static constexpr int RPP = NT / LPR;         // rows per pass of the workgroup
     static constexpr int R = D / RPP;            // rows held by each thread
     static constexpr int NW = NT / 64;           // waves
     static constexpr int LPE = D < 64 ? D : 64;  // lanes per log entry in the key-side pass
     static constexpr int EPW = 64 / LPE;         // log entries per wave and round
     static constexpr int CPL = D / LPE;          // key channels per lane
-    static_assert(D % 4 == 0 && NT % 64 == 0, "geometry");
+    static_assert(D % TV == 0 && TV % 4 == 0 && NT % 64 == 0, "geometry");
     static_assert(NT % LPR == 0 && D % RPP == 0 && R >= 1, "the tile must divide evenly");
-    static_assert(D <= NT, "one thread per value column in the column stage");
+    static_assert(TV <= NT, "one thread per value column in the column stage");
 };
 
+// Tile shape per head width: 32 KB (D = 128, two value tiles per head),
+// 16 KB (D = 64) and 4 KB (D = 32) per workgroup.
 template <int D>
-struct Threads {
-    static constexpr int value = D == 128 ? 256 : (D == 64 ? 128 : 64);
+struct Shape {
+    static constexpr int TV = D == 128 ? 64 : D;
+    static constexpr int NT = D == 128 ? 256 : (D == 64 ? 128 : 64);
 };
+
+// Workgroups are handed to the eight XCDs round-robin in dispatch order.
+// Map block b to (head, value tile) so that the tiles of one head are eight
+// blocks apart -- on the same XCD, where the second reads the head's shared
+// key-side log from that XCD's L2.
+__device__ __forceinline__ void block_to_tile(int b, int N, int ntile, int &n, int &tile) {
+    const int group = b / (8 * ntile);
+    const int within = b - group * 8 * ntile;
+    const int gs = min(8, N - group * 8);  // heads in this group (fewer in the last one)
+    tile = within / gs;
+    n = group * 8 + within % gs;
+}
 
 // Sum over aligned groups of W consecutive lanes.
 template <int W>
@@ -78,10 +97,10 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
-template <int OP, typename TIn, int D, int NT, int MODE, int CMAX>
+template <int OP, typename TIn, int D, int TV, int NT, int MODE, int CMAX>
 __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
-    using G = Geom<D, NT>;
-    constexpr int LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
+    using G = Geom<D, TV, NT>;
+    constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
     constexpr int LPE = G::LPE, EPW = G::EPW, CPL = G::CPL;
     constexpr bool DELTA = OP != OP_RWKV6;
     constexpr bool LOGGED = MODE != MODE_EAGER;  // reads a log
@@ -90,7 +109,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
     constexpr bool CUR_IN_LOG = MODE == MODE_MERGE && DELTA;  // fold the token as entry L
     constexpr int CP = LOGGED ? CMAX : 4;        // entry slots in LDS (multiple of 4)
     constexpr int KROUNDS = LOGGED ? (CMAX + NW * EPW - 1) / (NW * EPW) : 0;
-    constexpr int XROUNDS = LOGGED ? (CMAX * D + NT - 1) / NT : 0;
+    constexpr int XROUNDS = LOGGED ? (CMAX * TV + NT - 1) / NT : 0;
     using TX = typename std::conditional<DELTA, float, TIn>::type;  // value-side log dtype
     static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
 
@@ -100,26 +119,30 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
     __shared__ float s_krow[D];    // current key, per row
     __shared__ float s_wrow[D];    // RWKV6: current decay, per row
     __shared__ __attribute__((aligned(16))) float s_ktT[LOGGED ? D * CP : 4];  // [row][entry]
-    __shared__ __attribute__((aligned(16))) float s_x[LOGGED ? CP * D : 4];    // [entry][col]
+    __shared__ __attribute__((aligned(16))) float s_x[LOGGED ? CP * TV : 4];   // [entry][tile col]
     __shared__ float s_coef[2][CP];  // replay coefficients: k side, q/r side
-    __shared__ __attribute__((aligned(16))) float s_red[NW][2][D];
-    __shared__ __attribute__((aligned(16))) float s_u[D];  // current value factor
+    __shared__ __attribute__((aligned(16))) float s_red[NW][2][TV];
+    __shared__ __attribute__((aligned(16))) float s_u[TV];  // current value factor
     __shared__ float s_dot;          // <k,q> (delta rules) or sum r*bonus*k (RWKV6)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int n = blockIdx.x;
+    int n, tile;
+    block_to_tile(blockIdx.x, p.N, NTILE, n, tile);
     const int L = LOGGED ? p.L : 0;
     const int C = p.C;
-    const int cg = tid % LPR;  // float4 column group: columns 4cg .. 4cg+3
+    const int cg = tid % LPR;  // float4 column group: tile columns 4cg .. 4cg+3
     const int rs = tid / LPR;  // rows rs + RPP*i, i < R
+    const int col0 = tile * TV;  // first value column of the tile
 
     // 1. Issue the base tile loads first: they are nearly all of the traffic.
-    const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + (size_t)n * (D * D / 4);
+    //    Row r of the tile is TV/4 float4 at head offset r*D/4 + col0/4.
+    const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
+    const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
     f4 s[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + tid + NT * i);
+    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
 
     // 2. This lane's key channels c = lc + LPE*m: token inputs and log-decays.
     const int se = lane / LPE;
@@ -169,13 +192,14 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
             s_krow[c] = kc[m];
             s_wrow[c] = dc[m];
             if (LOGGED && CUR_IN_LOG) s_ktT[c * CP + L] = kc[m];
-            if (MODE == MODE_APPEND) {
+            if (MODE == MODE_APPEND && tile == 0) {
                 const size_t e = (size_t)n * C + L;
                 static_cast<TIn *>(p.logK)[e * D + c] = kin[c];
                 if (OP != OP_GDN) p.logG[e * D + c] = gnew[m];
             }
         }
-        if (MODE == MODE_APPEND && OP == OP_GDN && lane == 0) p.logG[(size_t)n * C + L] = gnew[0];
+        if (MODE == MODE_APPEND && OP == OP_GDN && tile == 0 && lane == 0)
+            p.logG[(size_t)n * C + L] = gnew[0];
     }
     if (TOKEN && wave == 0) {
         float part = 0.f;
@@ -221,12 +245,12 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
                 }
             }
         }
-        // Value side of the log, entries 0..L-1 (contiguous per head).
-        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D;
+        // Value side of the log: this tile's columns of entries 0..L-1.
+        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0;
 #pragma unroll
         for (int r = 0; r < XROUNDS; ++r) {
             const int idx = tid + NT * r;
-            if (idx < L * D) s_x[idx] = to_f32(xin[idx]);
+            if (idx < L * TV) s_x[idx] = to_f32(xin[(size_t)(idx / TV) * D + idx % TV]);
         }
         // Zero the slots between the last folded entry and the next multiple of four.
         if (WRITES) {
@@ -236,7 +260,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
                 const int i = ne + idx / D;
                 const int c = idx % D;
                 s_ktT[c * CP + i] = 0.f;
-                s_x[i * D + c] = 0.f;
+                if (c < TV) s_x[i * TV + c] = 0.f;
             }
         }
     }
@@ -270,18 +294,19 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
         }
         __syncthreads();
 
-        // 4. Column stage: one thread per value column.
-        if (tid < D) {
-            const int j = tid;
+        // 4. Column stage: one thread per value column of the tile.
+        if (tid < TV) {
+            const int jt = tid;        // column within the tile
+            const int j = col0 + jt;   // column within the head
             float yj = 0.f, zj = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
-                if (DELTA) yj += s_red[w][0][j];
-                zj += s_red[w][1][j];
+                if (DELTA) yj += s_red[w][0][jt];
+                zj += s_red[w][1][jt];
             }
             if (LOGGED) {
                 for (int i = 0; i < L; ++i) {
-                    const float x = s_x[i * D + j];
+                    const float x = s_x[i * TV + jt];
                     if (DELTA) yj += s_coef[0][i] * x;
                     zj += s_coef[1][i] * x;
                 }
@@ -305,9 +330,9 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
                     static_cast<TIn *>(p.logX)[e * D + j] = vraw;
             }
             if (LOGGED && CUR_IN_LOG)
-                s_x[L * D + j] = xnew;
+                s_x[L * TV + jt] = xnew;
             else
-                s_u[j] = xnew;
+                s_u[jt] = xnew;
         }
         if (WRITES) __syncthreads();
     }
@@ -321,10 +346,10 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
         for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rs + RPP * i];
         if (LOGGED) {
             for (int e = 0; e < ne; e += 4) {
-                const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * D + 4 * cg]);
-                const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * D + 4 * cg]);
-                const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * D + 4 * cg]);
-                const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * D + 4 * cg]);
+                const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + 4 * cg]);
+                const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + 4 * cg]);
+                const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + 4 * cg]);
+                const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + 4 * cg]);
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
                     const f4 kt = *reinterpret_cast<const f4 *>(&s_ktT[(rs + RPP * i) * CP + e]);
@@ -343,16 +368,17 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
                     acc[i] += s_krow[row] * u;
             }
         }
-        f4 *dst4 = reinterpret_cast<f4 *>(p.dst) + (size_t)n * (D * D / 4);
+        f4 *dst4 = reinterpret_cast<f4 *>(p.dst) + tile4;
 #pragma unroll
-        for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + tid + NT * i);
+        for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RPP * (D / 4));
     }
 }
 
 template <int OP, typename TIn, int D, int MODE, int CMAX>
 hipError_t launch_one(const StepParams &p, hipStream_t s) {
-    constexpr int NT = Threads<D>::value;
-    hipLaunchKernelGGL((step_kernel<OP, TIn, D, NT, MODE, CMAX>), dim3(p.N), dim3(NT), 0, s, p);
+    constexpr int TV = Shape<D>::TV, NT = Shape<D>::NT;
+    const unsigned blocks = (unsigned)p.N * (D / TV);
+    hipLaunchKernelGGL((step_kernel<OP, TIn, D, TV, NT, MODE, CMAX>), dim3(blocks), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 

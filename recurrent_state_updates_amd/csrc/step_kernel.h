@@ -47,26 +47,69 @@ namespace dlk {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint16_t bf16_bits;  // bfloat16 stored as its raw bits
 
+typedef unsigned int u2 __attribute__((ext_vector_type(2)));  // four packed bfloat16
+
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_bits b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Four consecutive input elements, loaded as one 16-byte (fp32) or 8-byte
+// (bf16) vector and unpacked to fp32.
+template <typename TIn>
+struct In4;
+template <>
+struct In4<float> {
+    typedef f4 raw;
+    __device__ static f4 unpack(f4 r) { return r; }
+};
+template <>
+struct In4<bf16_bits> {
+    typedef u2 raw;
+    __device__ static f4 unpack(u2 r) {
+        f4 o;
+        o.x = __uint_as_float(r.x << 16);
+        o.y = __uint_as_float(r.x & 0xffff0000u);
+        o.z = __uint_as_float(r.y << 16);
+        o.w = __uint_as_float(r.y & 0xffff0000u);
+        return o;
+    }
+};
+
+__device__ __forceinline__ float dot4(f4 a, f4 b) { return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w; }
+
+__device__ __forceinline__ f4 exp2v(f4 a) {
+    f4 o;
+    o.x = exp2f(a.x);
+    o.y = exp2f(a.y);
+    o.z = exp2f(a.z);
+    o.w = exp2f(a.w);
+    return o;
+}
+
+__device__ __forceinline__ f4 log2v(f4 a) {
+    f4 o;
+    o.x = log2f(a.x);
+    o.y = log2f(a.y);
+    o.z = log2f(a.z);
+    o.w = log2f(a.w);
+    return o;
 }
 
 // Thread geometry of one workgroup over a D x TV tile (all D key rows, TV of
 // the D value columns) of one head's state.
 template <int D, int TV, int NT>
 struct Geom {
-    static constexpr int NTILE = D / TV;         // value tiles per head
-    static constexpr int LPR = TV / 4;           // lanes per tile row (one float4 each)
-    static constexpr int RPP = NT / LPR;         // rows per pass of the workgroup
-    static constexpr int R = D / RPP;            // rows held by each thread
-    static constexpr int NW = NT / 64;           // waves
-    static constexpr int LPE = D < 64 ? D : 64;  // lanes per log entry in the key-side pass
-    static constexpr int EPW = 64 / LPE;         // log entries per wave and round
-    static constexpr int CPL = D / LPE;          // key channels per lane
+    static constexpr int NTILE = D / TV;  // value tiles per head
+    static constexpr int LPR = TV / 4;    // lanes per tile row (one float4 each)
+    static constexpr int RPP = NT / LPR;  // rows per pass of the workgroup
+    static constexpr int R = D / RPP;     // rows held by each thread
+    static constexpr int NW = NT / 64;    // waves
+    static constexpr int KL = D / 4;      // key-side lanes per log entry (4 channels each)
+    static constexpr int EPP = NT / KL;   // log entries per key-side pass
     static_assert(D % TV == 0 && TV % 4 == 0 && NT % 64 == 0, "geometry");
     static_assert(NT % LPR == 0 && D % RPP == 0 && R >= 1, "the tile must divide evenly");
-    static_assert(TV <= NT, "one thread per value column in the column stage");
+    static_assert(TV <= NT && KL <= 64 && NT % KL == 0, "column stage and key-side groups");
 };
 
 // Tile shape per head width: 32 KB (D = 128, two value tiles per head),
@@ -97,29 +140,50 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Optional occupancy floor in waves per SIMD (0: the compiler's choice).  A
+// floor that forces spills has been seen to place register copies inside a
+// lane-masked branch (the value of only the active lanes is kept), so the
+// default leaves the register budget to the compiler.
+#ifndef DLK_MIN_WAVES
+#define DLK_MIN_WAVES 0
+#endif
+#if DLK_MIN_WAVES > 0
+#define DLK_OCCUPANCY __attribute__((amdgpu_waves_per_eu(DLK_MIN_WAVES, 8)))
+#else
+#define DLK_OCCUPANCY
+#endif
+//
+// Structure: every global load the workgroup needs -- its base tile, the
+// token's inputs, the log entries (at clamped, always valid indices, masked
+// afterwards) and the value input of the column stage -- is issued first,
+// with no branch and no dependence between them, so that one memory
+// round-trip covers them all; only then does any arithmetic start.
 template <int OP, typename TIn, int D, int TV, int NT, int MODE, int CMAX>
-__global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
+__global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
+    const StepParams p) {
     using G = Geom<D, TV, NT>;
     constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
-    constexpr int LPE = G::LPE, EPW = G::EPW, CPL = G::CPL;
+    constexpr int KL = G::KL, EPP = G::EPP;
+    constexpr bool GDN = OP == OP_GDN;
     constexpr bool DELTA = OP != OP_RWKV6;
     constexpr bool LOGGED = MODE != MODE_EAGER;  // reads a log
     constexpr bool TOKEN = MODE != MODE_FOLD;    // decodes a token
     constexpr bool WRITES = MODE != MODE_APPEND; // writes a dense state
     constexpr bool CUR_IN_LOG = MODE == MODE_MERGE && DELTA;  // fold the token as entry L
     constexpr int CP = LOGGED ? CMAX : 4;        // entry slots in LDS (multiple of 4)
-    constexpr int KROUNDS = LOGGED ? (CMAX + NW * EPW - 1) / (NW * EPW) : 0;
-    constexpr int XROUNDS = LOGGED ? (CMAX * TV + NT - 1) / NT : 0;
+    constexpr int KPASS = LOGGED ? (CMAX + EPP - 1) / EPP : 1;
+    constexpr int XROUNDS = LOGGED ? (CMAX * TV + NT - 1) / NT : 1;
     using TX = typename std::conditional<DELTA, float, TIn>::type;  // value-side log dtype
+    using Raw = typename In4<TIn>::raw;
     static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
 
-    __shared__ float s_mv0[D];     // khat (delta rules)
-    __shared__ float s_mv1[D];     // qhat, or rhat (RWKV6)
-    __shared__ float s_scale[D];   // factor on each base row when a state is written
-    __shared__ float s_krow[D];    // current key, per row
-    __shared__ float s_wrow[D];    // RWKV6: current decay, per row
-    __shared__ __attribute__((aligned(16))) float s_ktT[LOGGED ? D * CP : 4];  // [row][entry]
-    __shared__ __attribute__((aligned(16))) float s_x[LOGGED ? CP * TV : 4];   // [entry][tile col]
+    __shared__ __attribute__((aligned(16))) float s_mv0[D];    // khat (delta rules)
+    __shared__ __attribute__((aligned(16))) float s_mv1[D];    // qhat, or rhat (RWKV6)
+    __shared__ __attribute__((aligned(16))) float s_scale[D];  // factor on each base row when writing
+    __shared__ __attribute__((aligned(16))) float s_krow[D];   // current key, per row
+    __shared__ __attribute__((aligned(16))) float s_wrow[D];   // RWKV6: current decay, per row
+    __shared__ __attribute__((aligned(16))) float s_kt[LOGGED ? CP * D : 4];  // [entry][row] decayed keys
+    __shared__ __attribute__((aligned(16))) float s_x[LOGGED ? CP * TV : 4];  // [entry][tile col]
     __shared__ float s_coef[2][CP];  // replay coefficients: k side, q/r side
     __shared__ __attribute__((aligned(16))) float s_red[NW][2][TV];
     __shared__ __attribute__((aligned(16))) float s_u[TV];  // current value factor
@@ -132,134 +196,172 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
     block_to_tile(blockIdx.x, p.N, NTILE, n, tile);
     const int L = LOGGED ? p.L : 0;
     const int C = p.C;
-    const int cg = tid % LPR;  // float4 column group: tile columns 4cg .. 4cg+3
-    const int rs = tid / LPR;  // rows rs + RPP*i, i < R
-    const int col0 = tile * TV;  // first value column of the tile
+    const int last = L > 0 ? L - 1 : 0;  // newest log entry (clamp target of masked loads)
+    const int cg = tid % LPR;            // float4 column group: tile columns 4cg .. 4cg+3
+    const int rs = tid / LPR;            // rows rs + RPP*i, i < R
+    const int col0 = tile * TV;          // first value column of the tile
+    const int c4 = 4 * (tid % KL);       // key-side work: channels c4 .. c4+3
+    const int ke = tid / KL;             //   of log entry pass*EPP + ke
 
-    // 1. Issue the base tile loads first: they are nearly all of the traffic.
-    //    Row r of the tile is TV/4 float4 at head offset r*D/4 + col0/4.
+    // ---------------- Phase A: issue every load ----------------
+    // A1. The base tile: nearly all of the traffic.  Row r of the tile is
+    //     TV/4 float4 at head offset r*D/4 + col0/4.
     const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
     const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
     f4 s[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
 
-    // 2. This lane's key channels c = lc + LPE*m: token inputs and log-decays.
-    const int se = lane / LPE;
-    const int lc = lane % LPE;
-    const TIn *kin = static_cast<const TIn *>(p.k) + (size_t)n * D;
-    const TIn *qin = static_cast<const TIn *>(p.q) + (size_t)n * D;
-    float kc[CPL], qc[CPL], dc[CPL], gnew[CPL], gref[CPL];
-    float alpha = 1.f, glast = 0.f;
-    if (OP == OP_GDN) {
-        if (TOKEN) alpha = p.decay[n];
-        if (LOGGED && L > 0) glast = p.logG[(size_t)n * C + (L - 1)];
+    // A2. The token: q (or r), k and the decay of channels c4..c4+3.
+    Raw kraw = {}, qraw = {};
+    f4 dec4 = {1.f, 1.f, 1.f, 1.f}, bon4 = {0.f, 0.f, 0.f, 0.f};
+    float alpha = 1.f, beta = 0.f;
+    TIn vraw = {};
+    if (TOKEN) {
+        kraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.k) + (size_t)n * D + c4);
+        qraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.q) + (size_t)n * D + c4);
+        if (GDN)
+            alpha = p.decay[n];
+        else
+            dec4 = *reinterpret_cast<const f4 *>(p.decay + (size_t)n * D + c4);
+        if (DELTA) beta = p.beta[n];
+        if (OP == OP_RWKV6) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
+        vraw = static_cast<const TIn *>(p.v)[(size_t)n * D + col0 + tid % TV];
     }
-#pragma unroll
-    for (int m = 0; m < CPL; ++m) {
-        const int c = lc + LPE * m;
-        kc[m] = 0.f;
-        qc[m] = 0.f;
-        dc[m] = 1.f;
-        if (TOKEN) {
-            kc[m] = to_f32(kin[c]);
-            qc[m] = to_f32(qin[c]);
-            dc[m] = (OP == OP_GDN) ? alpha : p.decay[(size_t)n * D + c];
-        }
-        float gl = glast;
-        if (OP != OP_GDN && LOGGED && L > 0) gl = p.logG[((size_t)n * C + (L - 1)) * D + c];
-        gnew[m] = gl + ((TOKEN && LOGGED) ? log2f(dc[m]) : 0.f);
-        gref[m] = (DELTA && TOKEN) ? gnew[m] : gl;
-    }
-
-    // Per-row factors, the current entry and the append of the key side
-    // (one writer per channel).
-    if (wave == 0 && se == 0) {
-#pragma unroll
-        for (int m = 0; m < CPL; ++m) {
-            const int c = lc + LPE * m;
-            float sc;
-            if (MODE == MODE_EAGER) {
-                sc = dc[m];
-                s_mv0[c] = dc[m] * kc[m];
-                s_mv1[c] = DELTA ? dc[m] * qc[m] : qc[m];  // RWKV6 reads the pre-update state
-            } else {
-                sc = exp2f(gref[m]);
-                s_mv0[c] = sc * kc[m];
-                s_mv1[c] = sc * qc[m];
-            }
-            s_scale[c] = sc;
-            s_krow[c] = kc[m];
-            s_wrow[c] = dc[m];
-            if (LOGGED && CUR_IN_LOG) s_ktT[c * CP + L] = kc[m];
-            if (MODE == MODE_APPEND && tile == 0) {
-                const size_t e = (size_t)n * C + L;
-                static_cast<TIn *>(p.logK)[e * D + c] = kin[c];
-                if (OP != OP_GDN) p.logG[e * D + c] = gnew[m];
-            }
-        }
-        if (MODE == MODE_APPEND && OP == OP_GDN && tile == 0 && lane == 0)
-            p.logG[(size_t)n * C + L] = gnew[0];
-    }
-    if (TOKEN && wave == 0) {
-        float part = 0.f;
-        if (se == 0) {
-#pragma unroll
-            for (int m = 0; m < CPL; ++m) {
-                const int c = lc + LPE * m;
-                part += DELTA ? kc[m] * qc[m] : qc[m] * p.bonus[(size_t)(n % p.H) * D + c] * kc[m];
-            }
-        }
-        part = group_sum<64>(part);
-        if (lane == 0) s_dot = part;
-    }
-
+    // A3. The log: cumulative log-decay of the newest entry, the key side of
+    //     this thread's entries and the tile's value side.
+    float glast_s = 0.f;
+    f4 glast4 = {0.f, 0.f, 0.f, 0.f};
+    Raw klog[KPASS];
+    float glog_s[KPASS];
+    f4 glog4[KPASS];
+    TX xraw[XROUNDS];
     if (LOGGED) {
-        // Key side of the log: decayed keys into LDS and, for a token, the
-        // replay coefficients <k_i 2^{g-g_i}, k_t> and <k_i 2^{g-g_i}, q_t>.
+        const size_t el = (size_t)n * C + last;
+        if (GDN)
+            glast_s = p.logG[el];
+        else
+            glast4 = *reinterpret_cast<const f4 *>(p.logG + el * D + c4);
 #pragma unroll
-        for (int r = 0; r < KROUNDS; ++r) {
-            const int i0 = (r * NW + wave) * EPW;  // wave-uniform
-            const int i = i0 + se;
-            const bool valid = i < L;
-            float pk = 0.f, pq = 0.f;
-#pragma unroll
-            for (int m = 0; m < CPL; ++m) {
-                const int c = lc + LPE * m;
-                if (valid) {
-                    const size_t e = (size_t)n * C + i;
-                    const float kv = to_f32(static_cast<const TIn *>(p.logK)[e * D + c]);
-                    const float gi = (OP == OP_GDN) ? p.logG[e] : p.logG[e * D + c];
-                    const float kt = kv * exp2f(gref[m] - gi);
-                    s_ktT[c * CP + i] = kt;
-                    pk += kt * kc[m];
-                    pq += kt * qc[m];
-                }
-            }
-            if (TOKEN && i0 < L) {
-                pk = group_sum<LPE>(pk);
-                pq = group_sum<LPE>(pq);
-                if (valid && lc == 0) {
-                    s_coef[0][i] = pk;
-                    s_coef[1][i] = pq;
-                }
-            }
+        for (int ps = 0; ps < KPASS; ++ps) {
+            const size_t e = (size_t)n * C + min(ps * EPP + ke, last);
+            klog[ps] = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.logK) + e * D + c4);
+            if (GDN)
+                glog_s[ps] = p.logG[e];
+            else
+                glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * D + c4);
         }
-        // Value side of the log: this tile's columns of entries 0..L-1.
         const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0;
 #pragma unroll
         for (int r = 0; r < XROUNDS; ++r) {
             const int idx = tid + NT * r;
-            if (idx < L * TV) s_x[idx] = to_f32(xin[(size_t)(idx / TV) * D + idx % TV]);
+            xraw[r] = xin[(size_t)min(idx / TV, last) * D + idx % TV];
         }
-        // Zero the slots between the last folded entry and the next multiple of four.
+    }
+
+    // ---------------- Phase B: key-side preparation into LDS ----------------
+    const f4 k = TOKEN ? In4<TIn>::unpack(kraw) : f4{0.f, 0.f, 0.f, 0.f};
+    const f4 q = TOKEN ? In4<TIn>::unpack(qraw) : f4{0.f, 0.f, 0.f, 0.f};
+    const f4 dv = GDN ? f4{alpha, alpha, alpha, alpha} : dec4;
+    f4 gl, gn, gref, sc;
+    if (GDN) {
+        const float g0 = L > 0 ? glast_s : 0.f;
+        const float g1 = g0 + ((TOKEN && LOGGED) ? log2f(alpha) : 0.f);
+        const float gr = (DELTA && TOKEN) ? g1 : g0;
+        const float e = MODE == MODE_EAGER ? alpha : exp2f(gr);
+        gl = f4{g0, g0, g0, g0};
+        gn = f4{g1, g1, g1, g1};
+        gref = f4{gr, gr, gr, gr};
+        sc = f4{e, e, e, e};
+    } else {
+        const f4 zero = {0.f, 0.f, 0.f, 0.f};
+        gl = L > 0 ? glast4 : zero;
+        gn = (TOKEN && LOGGED) ? gl + log2v(dec4) : gl;
+        gref = (DELTA && TOKEN) ? gn : gl;
+        sc = MODE == MODE_EAGER ? dec4 : exp2v(gref);
+    }
+    if (ke == 0) {
+        // per-row factors of the matrix-vector products and of the state write
+        f4 mv0, mv1;
+        if (MODE == MODE_EAGER) {
+            mv0 = dv * k;
+            mv1 = DELTA ? dv * q : q;  // RWKV6 reads the pre-update state
+        } else {
+            mv0 = sc * k;
+            mv1 = sc * q;
+        }
+        *reinterpret_cast<f4 *>(&s_mv0[c4]) = mv0;
+        *reinterpret_cast<f4 *>(&s_mv1[c4]) = mv1;
+        *reinterpret_cast<f4 *>(&s_scale[c4]) = sc;
+        *reinterpret_cast<f4 *>(&s_krow[c4]) = k;
+        *reinterpret_cast<f4 *>(&s_wrow[c4]) = dv;
+        if (LOGGED && CUR_IN_LOG) *reinterpret_cast<f4 *>(&s_kt[L * D + c4]) = k;
+    }
+    // append the token's key side as entry L (one writer per value; tile 0)
+    if (MODE == MODE_APPEND && tile == 0 && ke == 0) {
+        const size_t e = (size_t)n * C + L;
+        *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * D + c4) = kraw;
+        if (!GDN) *reinterpret_cast<f4 *>(p.logG + e * D + c4) = gn;
+    }
+    if (MODE == MODE_APPEND && GDN && tile == 0 && tid == 0) p.logG[(size_t)n * C + L] = gn.x;
+    if (TOKEN) {
+        // every key-side group holds all D channels, so each group's sum is complete
+        float part = DELTA ? dot4(k, q) : dot4(q * bon4, k);
+        part = group_sum<KL>(part);
+        if (tid == 0) s_dot = part;
+    }
+    if (LOGGED) {
+        // decayed keys k_i * 2^{g - g_i} and the replay coefficients
+        float pk[KPASS], pq[KPASS];
+#pragma unroll
+        for (int ps = 0; ps < KPASS; ++ps) {
+            const int i = ps * EPP + ke;
+            const bool valid = i < L;
+            const f4 kv = In4<TIn>::unpack(klog[ps]);
+            f4 kt;
+            if (GDN)
+                kt = kv * exp2f(gref.x - glog_s[ps]);
+            else
+                kt = kv * exp2v(gref - glog4[ps]);
+            if (!valid) kt = f4{0.f, 0.f, 0.f, 0.f};
+            pk[ps] = dot4(kt, k);
+            pq[ps] = dot4(kt, q);
+            if (WRITES && valid) *reinterpret_cast<f4 *>(&s_kt[i * D + c4]) = kt;
+        }
+        if (TOKEN) {
+#pragma unroll
+            for (int off = KL / 2; off >= 1; off >>= 1) {
+#pragma unroll
+                for (int ps = 0; ps < KPASS; ++ps) {
+                    pk[ps] += __shfl_xor(pk[ps], off);
+                    pq[ps] += __shfl_xor(pq[ps], off);
+                }
+            }
+            if (c4 == 0) {
+#pragma unroll
+                for (int ps = 0; ps < KPASS; ++ps) {
+                    const int i = ps * EPP + ke;
+                    if (i < L) {
+                        s_coef[0][i] = pk[ps];
+                        s_coef[1][i] = pq[ps];
+                    }
+                }
+            }
+        }
+        // value side of the log: this tile's columns of entries 0..L-1
+#pragma unroll
+        for (int r = 0; r < XROUNDS; ++r) {
+            const int idx = tid + NT * r;
+            if (idx < L * TV) s_x[idx] = to_f32(xraw[r]);
+        }
+        // zero the slots between the last folded entry and the next multiple of four
         if (WRITES) {
             const int ne = CUR_IN_LOG ? L + 1 : L;
             const int pad = ((ne + 3) & ~3) - ne;
             for (int idx = tid; idx < pad * D; idx += NT) {
                 const int i = ne + idx / D;
                 const int c = idx % D;
-                s_ktT[c * CP + i] = 0.f;
+                s_kt[i * D + c] = 0.f;
                 if (c < TV) s_x[i * TV + c] = 0.f;
             }
         }
@@ -267,7 +369,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
     __syncthreads();
 
     if (TOKEN) {
-        // 3. Matrix-vector products against the base tile held in registers.
+        // ---------------- Phase C: matrix-vector products ----------------
         f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -294,10 +396,10 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
         }
         __syncthreads();
 
-        // 4. Column stage: one thread per value column of the tile.
+        // ---------------- Phase D: column stage, one thread per tile column ----------------
         if (tid < TV) {
-            const int jt = tid;        // column within the tile
-            const int j = col0 + jt;   // column within the head
+            const int jt = tid;       // column within the tile
+            const int j = col0 + jt;  // column within the head
             float yj = 0.f, zj = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
@@ -311,11 +413,10 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
                     zj += s_coef[1][i] * x;
                 }
             }
-            const TIn vraw = static_cast<const TIn *>(p.v)[(size_t)n * D + j];
             const float vj = to_f32(vraw);
             float xnew, o;
             if (DELTA) {
-                xnew = p.beta[n] * (vj - yj);
+                xnew = beta * (vj - yj);
                 o = zj + s_dot * xnew;
             } else {
                 xnew = vj;
@@ -338,8 +439,9 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
     }
 
     if (WRITES) {
-        // 5. Write the state: row scale, rank-(entries) update from LDS, then
-        //    the current token for RWKV6 and the eager form.
+        // ---------------- Phase E: write the state ----------------
+        // row scale, the rank-(entries) update from LDS, then the current
+        // token for RWKV6 and the eager form.
         const int ne = CUR_IN_LOG ? L + 1 : L;
         f4 acc[R];
 #pragma unroll
@@ -352,8 +454,9 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepParams p) {
                 const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + 4 * cg]);
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    const f4 kt = *reinterpret_cast<const f4 *>(&s_ktT[(rs + RPP * i) * CP + e]);
-                    acc[i] += kt.x * x0 + kt.y * x1 + kt.z * x2 + kt.w * x3;
+                    const int row = rs + RPP * i;
+                    acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
+                              s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
                 }
             }
         }

@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--no-eager", action="store_true", help="skip the eager GPU kernel")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the CPU-baseline sample")
     ap.add_argument("--report", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 268 MB device-to-device copy (the reference kernel "
+                         "for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -116,21 +119,22 @@ def main():
     arg_refs = [ctypes.byref(a) for a in tok_args]
 
     def run_cycles(ncyc, tok0, marks=None):
-        """Launch ncyc merge cycles.  With marks, record three events per cycle:
-        before the first append, before the fold, after the fold."""
+        """Launch ncyc merge cycles.  With marks, record two events per cycle:
+        before its first launch and before its fold (the next cycle's first
+        event, or a final one, closes the fold)."""
         tok = tok0
         for c in range(ncyc):
             if marks is not None:
-                marks[c][0].record(stream)
+                marks[2 * c].record(stream)
             for i in range(C):
                 if marks is not None and i == C - 1:
-                    marks[c][1].record(stream)
+                    marks[2 * c + 1].record(stream)
                 rc = step_fn(handle, arg_refs[tok % T], sptr)
                 if rc != 0:
                     raise dl.DeltaLogError(rc, dl.dl_last_error())
                 tok += 1
-            if marks is not None:
-                marks[c][2].record(stream)
+        if marks is not None:
+            marks[2 * ncyc].record(stream)
         return tok
 
     # warm-up, then the timed region: K merge cycles, back-to-back launches,
@@ -138,7 +142,7 @@ def main():
     tok = run_cycles(args.warmup, 0)
     assert st.log_length == 0
     K = args.steps
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     tok = run_cycles(K, tok, marks)
@@ -146,8 +150,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_cycle = wall * 1e3 / K
     us_per_token = wall * 1e6 / (K * C)
-    appends = np.array([m[0].elapsed_time(m[1]) * 1e3 for m in marks])  # C-1 appends, back to back
-    folds = np.array([m[1].elapsed_time(m[2]) * 1e3 for m in marks])
+    appends = np.array([marks[2 * c].elapsed_time(marks[2 * c + 1]) * 1e3 for c in range(K)])
+    folds = np.array([marks[2 * c + 1].elapsed_time(marks[2 * c + 2]) * 1e3 for c in range(K)])
     kern_per_cycle = appends + folds
     us_tok_events = float(np.median(kern_per_cycle)) / C
 
@@ -236,6 +240,15 @@ def main():
                            "achieved_GBps": round(eb / (e_us * 1e-6) / 1e9, 1),
                            "model_MB_per_token": round(eb / 1e6, 2)}
         result["speedup_vs_eager"] = round(e_wall_us / us_per_token, 3)
+
+    if args.calibrate_copy:
+        src = torch.empty(sh.heads * D * D, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = int(src.numel() * 4)
+        del src, dst
 
     if args.cold:
         result["cold"] = cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs)

@@ -119,9 +119,9 @@ def main():
     arg_refs = [ctypes.byref(a) for a in tok_args]
 
     def run_cycles(ncyc, tok0, marks=None):
-        """Launch ncyc merge cycles.  With marks, record two events per cycle:
-        before its first launch and before its fold (the next cycle's first
-        event, or a final one, closes the fold)."""
+        """Launch ncyc merge cycles.  With marks (C > 1), record two events per
+        cycle: before its first launch and before its fold (the next cycle's
+        first event, or a final one, closes the fold)."""
         tok = tok0
         for c in range(ncyc):
             if marks is not None:
@@ -137,21 +137,34 @@ def main():
             marks[2 * ncyc].record(stream)
         return tok
 
-    # warm-up, then the timed region: K merge cycles, back-to-back launches,
-    # events only at the cycle boundaries and before each fold
+    # warm-up, then the timed region: K merge cycles of back-to-back launches
+    # with events at the cycle boundaries and before each fold (C = 1: only
+    # around the whole region, every launch being a fold)
     tok = run_cycles(args.warmup, 0)
     assert st.log_length == 0
     K = args.steps
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    tok = run_cycles(K, tok, marks)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if C > 1:
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K + 1)]
+        t0 = time.perf_counter()
+        tok = run_cycles(K, tok, marks)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        appends = np.array([marks[2 * c].elapsed_time(marks[2 * c + 1]) * 1e3 for c in range(K)])
+        folds = np.array([marks[2 * c + 1].elapsed_time(marks[2 * c + 2]) * 1e3 for c in range(K)])
+    else:
+        m0 = torch.cuda.Event(enable_timing=True)
+        m1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        m0.record(stream)
+        tok = run_cycles(K, tok)
+        m1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        appends = np.zeros(K)
+        folds = np.full(K, m0.elapsed_time(m1) * 1e3 / K)
     ms_per_cycle = wall * 1e3 / K
     us_per_token = wall * 1e6 / (K * C)
-    appends = np.array([marks[2 * c].elapsed_time(marks[2 * c + 1]) * 1e3 for c in range(K)])
-    folds = np.array([marks[2 * c + 1].elapsed_time(marks[2 * c + 2]) * 1e3 for c in range(K)])
     kern_per_cycle = appends + folds
     us_tok_events = float(np.median(kern_per_cycle)) / C
 

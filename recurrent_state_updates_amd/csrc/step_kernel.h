@@ -172,9 +172,10 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     constexpr bool CUR_IN_LOG = MODE == MODE_MERGE && DELTA;  // fold the token as entry L
     constexpr int CP = LOGGED ? CMAX : 4;        // entry slots in LDS (multiple of 4)
     constexpr int KPASS = LOGGED ? (CMAX + EPP - 1) / EPP : 1;
-    constexpr int XROUNDS = LOGGED ? (CMAX * TV + NT - 1) / NT : 1;
+    constexpr int XR = LOGGED ? (CMAX + RPP - 1) / RPP : 1;  // log value rows per thread
     using TX = typename std::conditional<DELTA, float, TIn>::type;  // value-side log dtype
     using Raw = typename In4<TIn>::raw;
+    using RawX = typename In4<TX>::raw;
     static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
 
     __shared__ __attribute__((aligned(16))) float s_mv0[D];    // khat (delta rules)
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     __shared__ __attribute__((aligned(16))) float s_krow[D];   // current key, per row
     __shared__ __attribute__((aligned(16))) float s_wrow[D];   // RWKV6: current decay, per row
     __shared__ __attribute__((aligned(16))) float s_kt[LOGGED ? CP * D : 4];  // [entry][row] decayed keys
-    __shared__ __attribute__((aligned(16))) float s_x[LOGGED ? CP * TV : 4];  // [entry][tile col]
+    __shared__ __attribute__((aligned(16))) float s_x[LOGGED && WRITES ? CP * TV : 4];  // [entry][tile col]
     __shared__ float s_coef[2][CP];  // replay coefficients: k side, q/r side
     __shared__ __attribute__((aligned(16))) float s_red[NW][2][TV];
     __shared__ __attribute__((aligned(16))) float s_u[TV];  // current value factor
@@ -204,15 +205,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     const int ke = tid / KL;             //   of log entry pass*EPP + ke
 
     // ---------------- Phase A: issue every load ----------------
-    // A1. The base tile: nearly all of the traffic.  Row r of the tile is
-    //     TV/4 float4 at head offset r*D/4 + col0/4.
-    const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
-    const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
-    f4 s[R];
-#pragma unroll
-    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
-
-    // A2. The token: q (or r), k and the decay of channels c4..c4+3.
+    // A1. The token: q (or r), k and the decay of channels c4..c4+3.
     Raw kraw = {}, qraw = {};
     f4 dec4 = {1.f, 1.f, 1.f, 1.f}, bon4 = {0.f, 0.f, 0.f, 0.f};
     float alpha = 1.f, beta = 0.f;
@@ -226,16 +219,17 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             dec4 = *reinterpret_cast<const f4 *>(p.decay + (size_t)n * D + c4);
         if (DELTA) beta = p.beta[n];
         if (OP == OP_RWKV6) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
-        vraw = static_cast<const TIn *>(p.v)[(size_t)n * D + col0 + tid % TV];
+        vraw = static_cast<const TIn *>(p.v)[(size_t)n * D + col0 + tid % TV];  // used by tid < TV
     }
-    // A3. The log: cumulative log-decay of the newest entry, the key side of
-    //     this thread's entries and the tile's value side.
+    // A2. The log: cumulative log-decay of the newest entry, the key side of
+    //     this thread's entries and, in the thread's own row slots (entries
+    //     rs + RPP*j), the tile's value side as float4 rows.
     float glast_s = 0.f;
     f4 glast4 = {0.f, 0.f, 0.f, 0.f};
     Raw klog[KPASS];
     float glog_s[KPASS];
     f4 glog4[KPASS];
-    TX xraw[XROUNDS];
+    RawX xrow[XR];
     if (LOGGED) {
         const size_t el = (size_t)n * C + last;
         if (GDN)
@@ -251,13 +245,21 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             else
                 glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * D + c4);
         }
-        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0;
+        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0 + 4 * cg;
 #pragma unroll
-        for (int r = 0; r < XROUNDS; ++r) {
-            const int idx = tid + NT * r;
-            xraw[r] = xin[(size_t)min(idx / TV, last) * D + idx % TV];
-        }
+        for (int j = 0; j < XR; ++j)
+            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * D);
     }
+
+    // A3. The base tile: nearly all of the traffic, issued last so that the
+    //     key-side preparation below, which waits only for the small loads
+    //     above (loads complete in issue order), overlaps the tile's flight.
+    //     Row r of the tile is TV/4 float4 at head offset r*D/4 + col0/4.
+    const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
+    const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
+    f4 s[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
 
     // ---------------- Phase B: key-side preparation into LDS ----------------
     const f4 k = TOKEN ? In4<TIn>::unpack(kraw) : f4{0.f, 0.f, 0.f, 0.f};
@@ -348,11 +350,13 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
                 }
             }
         }
-        // value side of the log: this tile's columns of entries 0..L-1
+        // value side of the log for the fold: this tile's columns of entries 0..L-1
+        if (WRITES) {
 #pragma unroll
-        for (int r = 0; r < XROUNDS; ++r) {
-            const int idx = tid + NT * r;
-            if (idx < L * TV) s_x[idx] = to_f32(xraw[r]);
+            for (int j = 0; j < XR; ++j) {
+                const int i = rs + RPP * j;
+                if (i < L) *reinterpret_cast<f4 *>(&s_x[i * TV + 4 * cg]) = In4<TX>::unpack(xrow[j]);
+            }
         }
         // zero the slots between the last folded entry and the next multiple of four
         if (WRITES) {
@@ -376,6 +380,19 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             const int row = rs + RPP * i;
             if (DELTA) y += s[i] * s_mv0[row];
             z += s[i] * s_mv1[row];
+        }
+        // the log replay joins the same reduction: entry i = rs + RPP*j adds
+        // coef_i * x_i to the partial sums of the thread holding row slot rs
+        if (LOGGED) {
+#pragma unroll
+            for (int j = 0; j < XR; ++j) {
+                const int i = rs + RPP * j;
+                if (i < L) {
+                    const f4 x = In4<TX>::unpack(xrow[j]);
+                    if (DELTA) y += s_coef[0][i] * x;
+                    z += s_coef[1][i] * x;
+                }
+            }
         }
 #pragma unroll
         for (int off = LPR; off < 64; off <<= 1) {
@@ -405,13 +422,6 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             for (int w = 0; w < NW; ++w) {
                 if (DELTA) yj += s_red[w][0][jt];
                 zj += s_red[w][1][jt];
-            }
-            if (LOGGED) {
-                for (int i = 0; i < L; ++i) {
-                    const float x = s_x[i * TV + jt];
-                    if (DELTA) yj += s_coef[0][i] * x;
-                    zj += s_coef[1][i] * x;
-                }
             }
             const float vj = to_f32(vraw);
             float xnew, o;

@@ -120,16 +120,18 @@ struct Shape {
     static constexpr int NT = D == 128 ? 256 : (D == 64 ? 128 : 64);
 };
 
-// Workgroups are handed to the eight XCDs round-robin in dispatch order.
-// Map block b to (head, value tile) so that the tiles of one head are eight
-// blocks apart -- on the same XCD, where the second reads the head's shared
-// key-side log from that XCD's L2.
+// Workgroups are handed to the eight XCDs round-robin in dispatch order
+// (block b runs on XCD b % 8).  Map block b so that each XCD walks one
+// contiguous range of (head, tile) pairs in order: the two tiles of a head
+// run back to back on the same XCD (the second reads the head's key-side
+// log from that XCD's L2), and each L2 gathers whole contiguous lines of the
+// outputs and log entries it writes instead of every eighth head's pieces.
 __device__ __forceinline__ void block_to_tile(int b, int N, int ntile, int &n, int &tile) {
-    const int group = b / (8 * ntile);
-    const int within = b - group * 8 * ntile;
-    const int gs = min(8, N - group * 8);  // heads in this group (fewer in the last one)
-    tile = within / gs;
-    n = group * 8 + within % gs;
+    const int nb = N * ntile;
+    const int x = b & 7, k = b >> 3;
+    const int g = x * (nb >> 3) + min(x, nb & 7) + k;  // XCD x owns pairs [off_x, off_x + count_x)
+    n = g / ntile;
+    tile = g - n * ntile;
 }
 
 // Sum over aligned groups of W consecutive lanes.

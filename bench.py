@@ -222,6 +222,37 @@ def main():
         "us_per_token_kernel_events": round(us_tok_events, 3),
         "us_per_token_without_events": round(us_per_token_noev, 3),
     }
+    # standalone fold (dl_merge mid-cycle) and materialise at L = C/2
+    if C > 1:
+        Lm = C // 2
+        while st.log_length != Lm:
+            rc = step_fn(handle, arg_refs[tok % T], sptr)
+            if rc != 0:
+                raise dl.DeltaLogError(rc, dl.dl_last_error())
+            tok += 1
+        dst = torch.empty_like(base)
+        reps = 10
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            dl.dl_materialize(handle, dst.data_ptr(), sptr)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mat_us = e0.elapsed_time(e1) * 1e3 / reps
+        e0.record(stream)
+        dl.dl_merge(handle, sptr)  # one early fold: L becomes 0
+        e1.record(stream)
+        torch.cuda.synchronize()
+        merge_only_us = e0.elapsed_time(e1) * 1e3
+        fb = traffic.fold_bytes(sh, Lm)
+        result["fold_kernels"] = {
+            "L": Lm, "materialize_us": round(mat_us, 2),
+            "materialize_GBps": round(fb / (mat_us * 1e-6) / 1e9, 1),
+            "merge_us": round(merge_only_us, 2),
+            "merge_GBps": round(fb / (merge_only_us * 1e-6) / 1e9, 1)}
+        del dst
     st.close()
     del st
 

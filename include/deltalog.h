@@ -145,6 +145,24 @@ int dl_log_length(const dl_state *h);
 dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *args,
                         void *stream);
 
+/* Modelled time per decode token (microseconds, amortised over one merge
+ * cycle of cfg->C tokens) from the per-launch traffic: each append moves the
+ * base, the token and the L entries it replays plus the entry it writes, at
+ * read_gbps; the token that fills the log moves the base twice, at copy_gbps
+ * (gist.science summary, "Modello di Traffico": appends of compact factors,
+ * one amortised dense write per interval, replay of the log).  Bandwidths
+ * <= 0 select the values these kernels sustain on MI355X (5900 GB/s read,
+ * 5750 GB/s read+write).  Host-only.  Returns a negative value for an
+ * invalid cfg. */
+double dl_predict_token_us(const dl_config *cfg, double read_gbps, double copy_gbps);
+
+/* The capacity C in [1, max_c] (max_c <= DL_MAX_CAPACITY) with the smallest
+ * dl_predict_token_us for cfg's other fields -- the interval that balances
+ * replay traffic against dense-write savings (gist.science, "Modello di
+ * Traffico").  Host-only.  Returns the C, or a negative dl_status for an
+ * invalid cfg or max_c. */
+int dl_choose_capacity(const dl_config *cfg, int max_c, double read_gbps, double copy_gbps);
+
 /* Release a handle (NULL is allowed).  Device buffers are not touched. */
 void dl_state_destroy(dl_state *h);
 

@@ -72,6 +72,8 @@ def load_library():
         "dl_log_length": (i, [vp]),
         "dl_eager_step": (i, [cp, vp, ap, vp]),
         "dl_state_destroy": (None, [vp]),
+        "dl_predict_token_us": (ctypes.c_double, [cp, ctypes.c_double, ctypes.c_double]),
+        "dl_choose_capacity": (i, [cp, i, ctypes.c_double, ctypes.c_double]),
         "dl_status_string": (ctypes.c_char_p, [i]),
         "dl_last_error": (ctypes.c_char_p, []),
     }
@@ -131,6 +133,20 @@ def dl_log_length(handle):
 
 def dl_eager_step(cfg, state, args, stream=0):
     _check(load_library().dl_eager_step(ctypes.byref(cfg), state, ctypes.byref(args), stream))
+
+
+def dl_predict_token_us(cfg, read_gbps=0.0, copy_gbps=0.0):
+    us = float(load_library().dl_predict_token_us(ctypes.byref(cfg), read_gbps, copy_gbps))
+    if us < 0:
+        raise DeltaLogError(DL_ERR_ARG, dl_last_error() or "invalid config")
+    return us
+
+
+def dl_choose_capacity(cfg, max_c=DL_MAX_CAPACITY, read_gbps=0.0, copy_gbps=0.0):
+    c = int(load_library().dl_choose_capacity(ctypes.byref(cfg), max_c, read_gbps, copy_gbps))
+    if c < 0:
+        _check(c)
+    return c
 
 
 def dl_state_destroy(handle):

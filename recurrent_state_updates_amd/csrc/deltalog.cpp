@@ -144,6 +144,24 @@ void set_log(dlk::StepParams &p, const dl_state *h) {
     p.L = h->L;
 }
 
+// Per-head bytes of the traffic model (mirrored by traffic.py for the bench).
+struct HeadBytes {
+    double base, token, out, entry, shared;
+};
+
+HeadBytes head_bytes(const dl_config *cfg) {
+    const double d = cfg->dk, s = (double)in_size(cfg->in_dtype);
+    HeadBytes b;
+    b.base = 4.0 * d * cfg->dv;
+    b.token = 2.0 * d * s + cfg->dv * s + (cfg->op != DL_RWKV6 ? 4.0 : 0.0) +
+              (cfg->op == DL_GDN ? 4.0 : 4.0 * d);
+    b.out = 4.0 * cfg->dv;
+    b.entry = (cfg->op == DL_RWKV6 ? cfg->dv * s : 4.0 * cfg->dv) + d * s +
+              (cfg->op == DL_GDN ? 4.0 : 4.0 * d);
+    b.shared = cfg->op == DL_RWKV6 ? 4.0 * d * cfg->H : 0.0;
+    return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,6 +274,40 @@ dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *
     p.base = state;
     p.dst = state;
     return launch(cfg, dlk::MODE_EAGER, p, stream);
+}
+
+double dl_predict_token_us(const dl_config *cfg, double read_gbps, double copy_gbps) {
+    size_t heads = 0;
+    if (check_config(cfg, &heads) != DL_OK) return -1.0;
+    if (read_gbps <= 0) read_gbps = 5900.0;
+    if (copy_gbps <= 0) copy_gbps = 5750.0;
+    const HeadBytes b = head_bytes(cfg);
+    const double n = (double)heads;
+    const int C = cfg->C;
+    double us = 0.0;
+    for (int L = 0; L + 1 < C; ++L)  // appends
+        us += (n * (b.base + b.token + b.out + (L + 1) * b.entry) + b.shared) / (read_gbps * 1e3);
+    us += (n * (2.0 * b.base + b.token + b.out + (C - 1) * b.entry) + b.shared) / (copy_gbps * 1e3);
+    return us / C;
+}
+
+int dl_choose_capacity(const dl_config *cfg, int max_c, double read_gbps, double copy_gbps) {
+    size_t heads = 0;
+    dl_status st = check_config(cfg, &heads);
+    if (st != DL_OK) return st;
+    if (max_c < 1 || max_c > DL_MAX_CAPACITY) return fail(DL_ERR_SHAPE, "max_c must lie in [1, 32]");
+    dl_config c = *cfg;
+    int best = 1;
+    double best_us = 0.0;
+    for (int C = 1; C <= max_c; ++C) {
+        c.C = C;
+        const double us = dl_predict_token_us(&c, read_gbps, copy_gbps);
+        if (C == 1 || us < best_us) {
+            best = C;
+            best_us = us;
+        }
+    }
+    return best;
 }
 
 void dl_state_destroy(dl_state *h) { delete h; }

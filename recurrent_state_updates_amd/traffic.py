@@ -6,7 +6,8 @@ token adds only O(dk + dv) numbers per head (gist.science summary, section
 with compact appends and one amortised dense write (section "Modello di
 Traffico").  These functions count the bytes each launch must move at
 minimum -- every input, log entry and state element read or written once --
-which is what "achieved GB/s" divides by.
+which is what "achieved GB/s" divides by.  The C library's
+dl_predict_token_us / dl_choose_capacity implement the same model.
 
 Per head, D = dk = dv, s = input element size (4 fp32, 2 bf16):
   base tile        4 D^2

@@ -136,8 +136,40 @@ dl_status dl_merge(dl_state *h, void *stream);
  * the handle, the base or the log.  dst must not be the base. */
 dl_status dl_materialize(const dl_state *h, float *dst, void *stream);
 
-/* Current log length L in [0, C), or -1 for a NULL handle. */
+/* Current log length L in [0, C) of a lockstep handle; -1 for a NULL or a
+ * per-slot handle (see dl_slot_log_length). */
 int dl_log_length(const dl_state *h);
+
+/* Per-slot logs (continuous batching).  The pages prepare replay
+ * coefficients per slot-head (gist.science summary, "Implementazione del
+ * Kernel") and serve many concurrent requests; here each of the B slots has
+ * its own log length, so requests may join and leave at any token.
+ *
+ * dl_state_init_slots is dl_state_init for such a handle, with every slot
+ * inactive; it enqueues one small kernel on `stream` (the workspace holds the
+ * per-slot bookkeeping).  On a per-slot handle:
+ *  - dl_decode_step decodes only active slots: a slot whose token fills its
+ *    log also folds it into its base in the same step; inactive slots' inputs
+ *    are ignored and their outputs left untouched;
+ *  - dl_merge folds every active slot's log (an early merge);
+ *  - dl_materialize writes the logical state of active slots only.
+ * Returns as for the lockstep calls. */
+dl_status dl_state_init_slots(dl_state **out, const dl_config *cfg, float *base, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Start a request in `slot` with an empty log: from the next decode step the
+ * slot's base block [H,dk,dv] is its dense state (the caller writes it before
+ * that step, in stream order).  DL_ERR_ARG for a bad slot or a lockstep
+ * handle. */
+dl_status dl_slot_activate(dl_state *h, int slot, void *stream);
+
+/* Stop decoding `slot` (its base and log stay as they are until the slot is
+ * activated again).  DL_ERR_ARG for a bad slot or a lockstep handle. */
+dl_status dl_slot_deactivate(dl_state *h, int slot, void *stream);
+
+/* Log length of an active slot in [0, C), or -1 for an inactive or invalid
+ * slot or a lockstep handle. */
+int dl_slot_log_length(const dl_state *h, int slot);
 
 /* The eager dense update for comparison (gist.science "Problema"): reads
  * the [B,H,dk,dv] fp32 state, writes out = o_t and the updated state in

@@ -72,6 +72,10 @@ def load_library():
         "dl_log_length": (i, [vp]),
         "dl_eager_step": (i, [cp, vp, ap, vp]),
         "dl_state_destroy": (None, [vp]),
+        "dl_state_init_slots": (i, [ctypes.POINTER(vp), cp, vp, vp, sz, vp]),
+        "dl_slot_activate": (i, [vp, i, vp]),
+        "dl_slot_deactivate": (i, [vp, i, vp]),
+        "dl_slot_log_length": (i, [vp, i]),
         "dl_predict_token_us": (ctypes.c_double, [cp, ctypes.c_double, ctypes.c_double]),
         "dl_choose_capacity": (i, [cp, i, ctypes.c_double, ctypes.c_double]),
         "dl_status_string": (ctypes.c_char_p, [i]),
@@ -113,6 +117,26 @@ def dl_state_init(cfg, base, workspace, workspace_bytes):
     _check(load_library().dl_state_init(ctypes.byref(h), ctypes.byref(cfg), base, workspace,
                                         workspace_bytes))
     return h.value
+
+
+def dl_state_init_slots(cfg, base, workspace, workspace_bytes, stream=0):
+    """Per-slot handle, every slot inactive; returns the handle (an integer)."""
+    h = ctypes.c_void_p()
+    _check(load_library().dl_state_init_slots(ctypes.byref(h), ctypes.byref(cfg), base, workspace,
+                                              workspace_bytes, stream))
+    return h.value
+
+
+def dl_slot_activate(handle, slot, stream=0):
+    _check(load_library().dl_slot_activate(handle, slot, stream))
+
+
+def dl_slot_deactivate(handle, slot, stream=0):
+    _check(load_library().dl_slot_deactivate(handle, slot, stream))
+
+
+def dl_slot_log_length(handle, slot):
+    return int(load_library().dl_slot_log_length(handle, slot))
 
 
 def dl_decode_step(handle, args, stream=0):

@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libdeltalog.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["deltalog.cpp", "kernels_gdn.hip", "kernels_kda.hip", "kernels_rwkv6.hip"]
+SOURCES = ["deltalog.cpp", "kernels_gdn.hip", "kernels_kda.hip", "kernels_rwkv6.hip", "slots.hip"]
 
 # Packed fp32 VALU ops are switched off for all device code; the host pass
 # prints that it does not know the feature, which is harmless.

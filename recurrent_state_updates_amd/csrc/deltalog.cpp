@@ -16,6 +16,7 @@
 #include <limits>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "launch.h"
 
@@ -25,7 +26,15 @@ struct dl_state {
     void *logX;
     void *logK;
     float *logG;
-    int L;
+    int L;  // lockstep log length
+    // per-slot logs (continuous batching): device arrays in the workspace and
+    // their host mirror; slot b's log length is (step - base[b]) mod C
+    bool slots;
+    int *slot_base;
+    unsigned char *slot_active;
+    std::vector<unsigned> h_base;
+    std::vector<unsigned char> h_active;
+    unsigned step;
 };
 
 namespace {
@@ -65,7 +74,7 @@ dl_status check_config(const dl_config *cfg, size_t *heads) {
 }
 
 struct Layout {
-    size_t x, k, g, total;
+    size_t x, k, g, sb, sa, total;
 };
 
 Layout layout_of(const dl_config *cfg, size_t heads) {
@@ -76,7 +85,9 @@ Layout layout_of(const dl_config *cfg, size_t heads) {
     l.x = 0;
     l.k = round_up(entries * cfg->dv * xs, 256);
     l.g = l.k + round_up(entries * cfg->dk * in_size(cfg->in_dtype), 256);
-    l.total = l.g + round_up(entries * gw * 4, 256);
+    l.sb = l.g + round_up(entries * gw * 4, 256);            // per-slot log origin [B] int32
+    l.sa = l.sb + round_up((size_t)cfg->B * 4, 256);         // per-slot active flag [B] uint8
+    l.total = l.sa + round_up((size_t)cfg->B, 256);
     return l;
 }
 
@@ -142,6 +153,59 @@ void set_log(dlk::StepParams &p, const dl_state *h) {
     p.logK = h->logK;
     p.logG = h->logG;
     p.L = h->L;
+    if (h->slots) {
+        p.slot_base = h->slot_base;
+        p.slot_active = h->slot_active;
+        p.step = h->step;
+    }
+}
+
+int slot_length(const dl_state *h, int b) { return (int)((h->step - h->h_base[b]) % (unsigned)h->cfg.C); }
+
+dl_status slot_set(dl_state *h, int slot, int set_base, int base_value, int set_active, int active_value,
+                   int only_active, void *stream) {
+    const hipError_t e = dlk::launch_slot_set(h->slot_base, h->slot_active, h->cfg.B, slot, set_base, base_value,
+                                              set_active, active_value, only_active,
+                                              static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DL_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+    return DL_OK;
+}
+
+dl_status init_handle(dl_state **out, const dl_config *cfg, float *base, void *workspace,
+                      size_t workspace_bytes, bool slots) {
+    if (!out) return fail(DL_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    size_t heads = 0;
+    dl_status st = check_config(cfg, &heads);
+    if (st != DL_OK) return st;
+    if (!base || !workspace) return fail(DL_ERR_ARG, "base and workspace must be non-NULL");
+    if (!aligned16(base) || !aligned16(workspace))
+        return fail(DL_ERR_ARG, "base and workspace must be 16-byte aligned");
+    const Layout l = layout_of(cfg, heads);
+    if (workspace_bytes < l.total)
+        return fail(DL_ERR_WORKSPACE, "workspace is smaller than dl_workspace_bytes(cfg) = " +
+                                          std::to_string(l.total));
+    dl_state *h = new (std::nothrow) dl_state;
+    if (!h) return fail(DL_ERR_ARG, "out of host memory");
+    char *ws = static_cast<char *>(workspace);
+    h->cfg = *cfg;
+    h->base = base;
+    h->logX = ws + l.x;
+    h->logK = ws + l.k;
+    h->logG = reinterpret_cast<float *>(ws + l.g);
+    h->L = 0;
+    h->slots = slots;
+    h->slot_base = reinterpret_cast<int *>(ws + l.sb);
+    h->slot_active = reinterpret_cast<unsigned char *>(ws + l.sa);
+    h->step = 0;
+    if (slots) {
+        h->h_base.assign(cfg->B, 0u);
+        h->h_active.assign(cfg->B, 0);
+    }
+    *out = h;
+    g_last_error.clear();
+    return DL_OK;
 }
 
 // Per-head bytes of the traffic model (mirrored by traffic.py for the bench).
@@ -186,30 +250,43 @@ dl_status dl_workspace_layout(const dl_config *cfg, size_t offsets[3]) {
 
 dl_status dl_state_init(dl_state **out, const dl_config *cfg, float *base, void *workspace,
                         size_t workspace_bytes) {
-    if (!out) return fail(DL_ERR_ARG, "out is NULL");
-    *out = nullptr;
-    size_t heads = 0;
-    dl_status st = check_config(cfg, &heads);
+    return init_handle(out, cfg, base, workspace, workspace_bytes, false);
+}
+
+dl_status dl_state_init_slots(dl_state **out, const dl_config *cfg, float *base, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    dl_status st = init_handle(out, cfg, base, workspace, workspace_bytes, true);
     if (st != DL_OK) return st;
-    if (!base || !workspace) return fail(DL_ERR_ARG, "base and workspace must be non-NULL");
-    if (!aligned16(base) || !aligned16(workspace))
-        return fail(DL_ERR_ARG, "base and workspace must be 16-byte aligned");
-    const Layout l = layout_of(cfg, heads);
-    if (workspace_bytes < l.total)
-        return fail(DL_ERR_WORKSPACE, "workspace is smaller than dl_workspace_bytes(cfg) = " +
-                                          std::to_string(l.total));
-    dl_state *h = new (std::nothrow) dl_state;
-    if (!h) return fail(DL_ERR_ARG, "out of host memory");
-    char *ws = static_cast<char *>(workspace);
-    h->cfg = *cfg;
-    h->base = base;
-    h->logX = ws + l.x;
-    h->logK = ws + l.k;
-    h->logG = reinterpret_cast<float *>(ws + l.g);
-    h->L = 0;
-    *out = h;
-    g_last_error.clear();
+    st = slot_set(*out, -1, 1, 0, 1, 0, 0, stream);  // every slot inactive, origin 0
+    if (st != DL_OK) {
+        delete *out;
+        *out = nullptr;
+    }
+    return st;
+}
+
+dl_status dl_slot_activate(dl_state *h, int slot, void *stream) {
+    if (!h || !h->slots) return fail(DL_ERR_ARG, "handle is NULL or not a per-slot handle");
+    if (slot < 0 || slot >= h->cfg.B) return fail(DL_ERR_ARG, "slot out of range");
+    dl_status st = slot_set(h, slot, 1, (int)h->step, 1, 1, 0, stream);
+    if (st != DL_OK) return st;
+    h->h_base[slot] = h->step;
+    h->h_active[slot] = 1;
     return DL_OK;
+}
+
+dl_status dl_slot_deactivate(dl_state *h, int slot, void *stream) {
+    if (!h || !h->slots) return fail(DL_ERR_ARG, "handle is NULL or not a per-slot handle");
+    if (slot < 0 || slot >= h->cfg.B) return fail(DL_ERR_ARG, "slot out of range");
+    dl_status st = slot_set(h, slot, 0, 0, 1, 0, 0, stream);
+    if (st != DL_OK) return st;
+    h->h_active[slot] = 0;
+    return DL_OK;
+}
+
+int dl_slot_log_length(const dl_state *h, int slot) {
+    if (!h || !h->slots || slot < 0 || slot >= h->cfg.B || !h->h_active[slot]) return -1;
+    return slot_length(h, slot);
 }
 
 dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
@@ -223,6 +300,21 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
     set_log(p, h);
     set_token(p, a);
     p.dst = h->base;
+    if (h->slots) {
+        // each active slot appends, or decodes and folds when its token fills its log
+        bool any_append = false, any_fold = false;
+        for (int b = 0; b < h->cfg.B; ++b) {
+            if (!h->h_active[b]) continue;
+            if (slot_length(h, b) + 1 == h->cfg.C)
+                any_fold = true;
+            else
+                any_append = true;
+        }
+        if (any_append && (st = launch(&h->cfg, dlk::MODE_APPEND, p, stream)) != DL_OK) return st;
+        if (any_fold && (st = launch(&h->cfg, dlk::MODE_MERGE, p, stream)) != DL_OK) return st;
+        ++h->step;
+        return DL_OK;
+    }
     const bool fold = h->L + 1 == h->cfg.C;
     st = launch(&h->cfg, fold ? dlk::MODE_MERGE : dlk::MODE_APPEND, p, stream);
     if (st != DL_OK) return st;
@@ -232,10 +324,24 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
 
 dl_status dl_merge(dl_state *h, void *stream) {
     if (!h) return fail(DL_ERR_ARG, "handle is NULL");
-    if (h->L == 0) return DL_OK;
     size_t heads = 0;
     dl_status st = check_config(&h->cfg, &heads);
     if (st != DL_OK) return st;
+    if (h->slots) {
+        bool any = false;
+        for (int b = 0; b < h->cfg.B; ++b) any = any || (h->h_active[b] && slot_length(h, b) > 0);
+        if (!any) return DL_OK;
+        dlk::StepParams p = params_of(&h->cfg, heads);
+        set_log(p, h);
+        p.dst = h->base;
+        if ((st = launch(&h->cfg, dlk::MODE_FOLD, p, stream)) != DL_OK) return st;
+        // every active slot's log is now empty: its origin moves to this step
+        if ((st = slot_set(h, -1, 1, (int)h->step, 0, 0, 1, stream)) != DL_OK) return st;
+        for (int b = 0; b < h->cfg.B; ++b)
+            if (h->h_active[b]) h->h_base[b] = h->step;
+        return DL_OK;
+    }
+    if (h->L == 0) return DL_OK;
     dlk::StepParams p = params_of(&h->cfg, heads);
     set_log(p, h);
     p.dst = h->base;
@@ -259,7 +365,7 @@ dl_status dl_materialize(const dl_state *h, float *dst, void *stream) {
     return launch(&h->cfg, dlk::MODE_FOLD, p, stream);
 }
 
-int dl_log_length(const dl_state *h) { return h ? h->L : -1; }
+int dl_log_length(const dl_state *h) { return (h && !h->slots) ? h->L : -1; }
 
 dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *a, void *stream) {
     size_t heads = 0;

@@ -31,6 +31,12 @@ struct StepParams {
     int C;               // log capacity (entry stride of the log arrays)
     int H;               // heads per slot (bonus row = n % H)
     int N;               // heads = grid size
+    // Per-slot logs (continuous batching); slot_base == nullptr selects the
+    // lockstep log of length L.  Slot b's log length is
+    // (step - slot_base[b]) mod C; inactive slots are skipped.
+    const int *slot_base;              // [B] decode-step index of the slot's last empty log
+    const unsigned char *slot_active;  // [B] 1 = decode this slot
+    unsigned step;                     // decode steps issued so far
 };
 
 // Launch one mode for one operator.  in_bf16 selects the input dtype, D the
@@ -38,5 +44,11 @@ struct StepParams {
 hipError_t launch_gdn(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
 hipError_t launch_kda(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
 hipError_t launch_rwkv6(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
+
+// Set slot_base / slot_active entries: slot < 0 means every slot (with
+// only_active, every active slot); set_base / set_active select the fields.
+hipError_t launch_slot_set(int *slot_base, unsigned char *slot_active, int B, int slot, int set_base,
+                           int base_value, int set_active, int active_value, int only_active,
+                           hipStream_t s);
 
 }  // namespace dlk

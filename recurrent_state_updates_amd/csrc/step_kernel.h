@@ -197,8 +197,18 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     const int wave = tid >> 6;
     int n, tile;
     block_to_tile(blockIdx.x, p.N, NTILE, n, tile);
-    const int L = LOGGED ? p.L : 0;
     const int C = p.C;
+    int L = LOGGED ? p.L : 0;
+    if (LOGGED && p.slot_base != nullptr) {
+        // per-slot logs: this slot's own length; a decode step launches the
+        // append for slots that stay below C and the fold for slots that fill
+        // (the whole workgroup leaves together, before any barrier)
+        const int b = n / p.H;
+        if (!p.slot_active[b]) return;
+        L = (int)((p.step - (unsigned)p.slot_base[b]) % (unsigned)C);
+        if (MODE == MODE_APPEND && L + 1 == C) return;
+        if (MODE == MODE_MERGE && L + 1 != C) return;
+    }
     const int last = L > 0 ? L - 1 : 0;  // newest log entry (clamp target of masked loads)
     const int cg = tid % LPR;            // float4 column group: tile columns 4cg .. 4cg+3
     const int rs = tid / LPR;            // rows rs + RPP*i, i < R

@@ -60,10 +60,12 @@ class DeltaLogState:
     """A base state plus its log workspace, driven through dl_decode_step.
 
     ``base`` is a caller-owned [B, H, d, d] fp32 CUDA tensor; it is updated in
-    place at every fold.  The workspace is allocated here with torch.
+    place at every fold.  The workspace is allocated here with torch.  With
+    ``slots=True`` every slot keeps its own log length (continuous batching):
+    slots start inactive and are switched with ``activate`` / ``deactivate``.
     """
 
-    def __init__(self, op, in_dtype, base, C):
+    def __init__(self, op, in_dtype, base, C, slots=False):
         if op not in B.OP_CODES or in_dtype not in B.DTYPE_CODES:
             raise ValueError(f"unknown op {op!r} or dtype {in_dtype!r}")
         if base.dim() != 4:
@@ -78,7 +80,12 @@ class DeltaLogState:
         nbytes = B.dl_workspace_bytes(self.cfg)
         self.base = base
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
-        self.handle = B.dl_state_init(self.cfg, base.data_ptr(), self.workspace.data_ptr(), nbytes)
+        self.slots = bool(slots)
+        if self.slots:
+            self.handle = B.dl_state_init_slots(self.cfg, base.data_ptr(), self.workspace.data_ptr(), nbytes,
+                                                _stream(self.device))
+        else:
+            self.handle = B.dl_state_init(self.cfg, base.data_ptr(), self.workspace.data_ptr(), nbytes)
 
     def step(self, q, k, v, beta, decay, bonus=None, out=None):
         """Decode one token for all heads; returns out [B, H, dv] fp32."""
@@ -110,6 +117,15 @@ class DeltaLogState:
     @property
     def log_length(self):
         return B.dl_log_length(self.handle)
+
+    def activate(self, slot):
+        B.dl_slot_activate(self.handle, slot, _stream(self.device))
+
+    def deactivate(self, slot):
+        B.dl_slot_deactivate(self.handle, slot, _stream(self.device))
+
+    def slot_log_length(self, slot):
+        return B.dl_slot_log_length(self.handle, slot)
 
     def workspace_views(self):
         """(X, K, G) views of the log for inspection: [B,H,C,dv], [B,H,C,dk], [B,H,C(,dk)]."""

@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), f"{name} is declared in deltalog.h but not exported"
     for name in names:
@@ -67,7 +67,8 @@ def test_workspace_size_and_layout(op, dtype, d, C):
     x = _round(n * d * xsz)
     k = _round(n * d * isz)
     g = _round(n * gw * 4)
-    assert dl.dl_workspace_bytes(cfg) == x + k + g
+    slots = _round(Bsz * 4) + _round(Bsz)  # per-slot log origin and active flag
+    assert dl.dl_workspace_bytes(cfg) == x + k + g + slots
     assert dl.dl_workspace_layout(cfg) == (0, x, x + k)
 
 
@@ -148,6 +149,27 @@ def test_decode_step_rejects_bad_args_without_state_change(op, over):
         dl.dl_state_destroy(h)
     lib = B.load_library()
     assert lib.dl_decode_step(None, ctypes.byref(_args()), None) == B.DL_ERR_ARG
+
+
+def test_slot_calls_validate_on_the_host():
+    cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)
+    lib = B.load_library()
+    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    try:
+        # a lockstep handle has no slots
+        with pytest.raises(dl.DeltaLogError):
+            dl.dl_slot_activate(h, 0)
+        with pytest.raises(dl.DeltaLogError):
+            dl.dl_slot_deactivate(h, 0)
+        assert dl.dl_slot_log_length(h, 0) == -1
+    finally:
+        dl.dl_state_destroy(h)
+    # init_slots validates before enqueueing anything
+    with pytest.raises(dl.DeltaLogError):
+        dl.dl_state_init_slots(cfg, FAKE, FAKE, 16)
+    with pytest.raises(dl.DeltaLogError):
+        dl.dl_state_init_slots(B.Config(0, 1, 0, 4, 64, 64, 4), FAKE, FAKE, 1 << 20)
+    assert lib.dl_slot_log_length(None, 0) == -1
 
 
 def test_eager_step_rejects_bad_state():

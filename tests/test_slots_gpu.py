@@ -1,0 +1,112 @@
+"""Per-slot logs (continuous batching) on the GPU, against the fp64 oracle.
+
+Slots join and leave at different tokens, so each slot's log length differs
+from the others'; every active slot's outputs and state must still equal the
+eager recurrence of that slot's own token sequence from its own start state.
+"""
+import numpy as np
+import pytest
+import torch
+
+import recurrent_state_updates_amd as dl
+import workloads
+from tests import gpu_support as gs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu tests must run on an MI355X")
+    dl.load_library()
+    yield
+
+
+def _token(dev, t):
+    return gs._token(dev, t)
+
+
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_all_slots_together_equals_lockstep(op):
+    T, Bsz, H, d, C = 13, 3, 2, 128, 4
+    x = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=31)
+    dev = gs.to_device(x, DEV)
+    lock, _, _ = gs.run_deltalog(dev, op, "bf16", C)
+    base = dev["S0"].clone()
+    st = dl.DeltaLogState(op, "bf16", base, C, slots=True)
+    for b in range(Bsz):
+        st.activate(b)
+    outs = torch.empty_like(lock)
+    for t in range(T):
+        st.step(out=outs[t], **_token(dev, t))
+        assert all(st.slot_log_length(b) == (t + 1) % C for b in range(Bsz))
+    torch.cuda.synchronize()
+    assert torch.equal(outs, lock)
+
+
+def _segment_reference(x, op, slot, H, start, end, S0_seg, chk_end):
+    """Oracle of one slot's heads over tokens [start, end) from S0_seg [H, d, d]."""
+    sl = {}
+    for key in ("q", "k", "v", "beta", "decay"):
+        sl[key] = None if x[key] is None else x[key][start:end, slot:slot + 1]
+    sl["bonus"] = x["bonus"]
+    sl["S0"] = S0_seg[None]
+    return gs.oracle_run(sl, op, chk_steps=[end - start] if chk_end else [])
+
+
+@pytest.mark.parametrize("op,C", [("gdn", 4), ("kda", 3), ("rwkv6", 4), ("gdn", 1), ("kda", 8)])
+def test_continuous_batching_schedule(op, C):
+    T, Bsz, H, d = 24, 5, 2, 64
+    x = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=41 + C)
+    dev = gs.to_device(x, DEV)
+    # slot -> list of [start, end) active segments
+    segments = {0: [(0, 24)], 1: [(1, 10), (13, 24)], 2: [(2, 24)], 3: [(5, 19)], 4: [(7, 24)]}
+    g = torch.Generator().manual_seed(7 + C)
+    seg_S0 = {(b, s): torch.randn((H, d, d), generator=g) * 0.02 for b, segs in segments.items()
+              for s, _ in segs}
+    base = torch.zeros((Bsz, H, d, d), dtype=torch.float32, device=DEV)
+    st = dl.DeltaLogState(op, "bf16", base, C, slots=True)
+    outs = torch.full((T, Bsz, H, d), float("nan"), dtype=torch.float32, device=DEV)
+    merge_after = {11, 17}
+    expect = {}  # slot -> expected log length while active
+    for t in range(T):
+        for b, segs in segments.items():
+            for s, e in segs:
+                if e == t:
+                    st.deactivate(b)
+                    expect.pop(b, None)
+                if s == t:
+                    base[b].copy_(seg_S0[(b, s)].to(DEV))
+                    st.activate(b)
+                    expect[b] = 0
+        st.step(out=outs[t], **_token(dev, t))
+        for b in expect:
+            expect[b] = (expect[b] + 1) % C
+        if t + 1 in merge_after:
+            st.merge()
+            for b in expect:
+                expect[b] = 0
+        for b in range(Bsz):
+            assert st.slot_log_length(b) == expect.get(b, -1), (t, b)
+    final = st.materialize(torch.full_like(base, float("nan")))
+    torch.cuda.synchronize()
+    o = outs.cpu().numpy()
+    fin = final.cpu().numpy()
+    for b, segs in segments.items():
+        for s, e in segs:
+            ref = _segment_reference(x, op, b, H, s, e, seg_S0[(b, s)], chk_end=(e == T))
+            got = o[s:e, b]  # [steps, H, d]
+            worst = max(gs.rel(got[i], ref["out"][i]) for i in range(e - s))
+            assert worst <= gs.OUT_GATE, (b, s, e, worst)
+            if e == T:
+                assert gs.rel(fin[b], ref["states"][0]) <= gs.STATE_GATE
+        # steps where the slot was inactive keep the untouched (NaN) output
+        active = np.zeros(T, dtype=bool)
+        for s, e in segs:
+            active[s:e] = True
+        assert np.isnan(o[~active, b]).all()
+    # slot 3 ended before T: materialise leaves inactive slots untouched
+    assert np.isnan(fin[3]).all()

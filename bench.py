@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--no-eager", action="store_true", help="skip the eager GPU kernel")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the CPU-baseline sample")
     ap.add_argument("--report", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--staggered", action="store_true",
+                    help="also time per-slot logs with slot b starting at token b mod C, so that "
+                         "1/C of the slots fold at every step (continuous batching)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 268 MB device-to-device copy (the reference kernel "
                          "for scaling hardware byte counters)")
@@ -288,6 +291,9 @@ def main():
                            "model_MB_per_token": round(eb / 1e6, 2)}
         result["speedup_vs_eager"] = round(e_wall_us / us_per_token, 3)
 
+    if args.staggered and C > 1:
+        result["staggered"] = staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K)
+
     if args.calibrate_copy:
         src = torch.empty(sh.heads * D * D, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -308,6 +314,49 @@ def main():
     if args.report:
         with open(args.report, "a") as f:
             f.write(line + "\n")
+
+
+def staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K):
+    """Per-slot logs, slot b started at token b mod C: every step then folds
+    the 1/C of the slots whose log fills and appends for the rest."""
+    import ctypes
+    import numpy as np
+    import torch
+    base = d["S0"].clone()
+    st = dl.DeltaLogState(w.op, w.in_dtype, base, C, slots=True)
+    T = w.T
+    args = [ctypes.byref(st.step_args(d["q"][t], d["k"][t], d["v"][t],
+                                      None if d["beta"] is None else d["beta"][t], d["decay"][t],
+                                      d["bonus"], outs[t])) for t in range(T)]
+    fn = dl.load_library().dl_decode_step
+    sptr = stream.cuda_stream
+    tok = 0
+    for s_ in range(C):  # staggered starts
+        for b in range(s_, Bsz, C):
+            st.activate(b)
+        assert fn(st.handle, args[tok % T], sptr) == 0
+        tok += 1
+    for _ in range(3 * C):
+        assert fn(st.handle, args[tok % T], sptr) == 0
+        tok += 1
+    steps = K * C
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        assert fn(st.handle, args[tok % T], sptr) == 0
+        tok += 1
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) * 1e6 / steps
+    ev_us = e0.elapsed_time(e1) * 1e3 / steps
+    st.close()
+    tok_bytes = traffic.per_token_bytes(sh, C)
+    return {"us_per_token": round(wall_us, 3), "events_us_per_token": round(ev_us, 3),
+            "achieved_GBps": round(tok_bytes / (wall_us * 1e-6) / 1e9, 1),
+            "note": "one launch per step; each slot appends, or folds when its token fills its log"}
 
 
 def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs):

@@ -301,17 +301,11 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
     set_token(p, a);
     p.dst = h->base;
     if (h->slots) {
-        // each active slot appends, or decodes and folds when its token fills its log
-        bool any_append = false, any_fold = false;
-        for (int b = 0; b < h->cfg.B; ++b) {
-            if (!h->h_active[b]) continue;
-            if (slot_length(h, b) + 1 == h->cfg.C)
-                any_fold = true;
-            else
-                any_append = true;
-        }
-        if (any_append && (st = launch(&h->cfg, dlk::MODE_APPEND, p, stream)) != DL_OK) return st;
-        if (any_fold && (st = launch(&h->cfg, dlk::MODE_MERGE, p, stream)) != DL_OK) return st;
+        // one launch: each active slot appends, or decodes and folds when its
+        // token fills its log (its workgroups choose at run time)
+        bool any = false;
+        for (int b = 0; b < h->cfg.B; ++b) any = any || h->h_active[b];
+        if (any && (st = launch(&h->cfg, dlk::MODE_AUTO, p, stream)) != DL_OK) return st;
         ++h->step;
         return DL_OK;
     }

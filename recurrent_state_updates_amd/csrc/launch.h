@@ -12,7 +12,8 @@ enum { OP_GDN = 0, OP_KDA = 1, OP_RWKV6 = 2 };
 //   MERGE   decode a token (L = C-1 entries logged) and fold all C into the base
 //   EAGER   decode a token directly on a dense state (no log), rewrite it
 //   FOLD    write base + log (L entries) to dst; no token
-enum { MODE_APPEND = 0, MODE_MERGE = 1, MODE_EAGER = 2, MODE_FOLD = 3 };
+//   AUTO    per slot: APPEND, or MERGE when the token fills the slot's log
+enum { MODE_APPEND = 0, MODE_MERGE = 1, MODE_EAGER = 2, MODE_FOLD = 3, MODE_AUTO = 4 };
 
 struct StepParams {
     float *base;         // [N][D][D] fp32 base (or dense state for EAGER)

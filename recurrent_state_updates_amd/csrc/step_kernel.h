@@ -170,8 +170,8 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     constexpr bool DELTA = OP != OP_RWKV6;
     constexpr bool LOGGED = MODE != MODE_EAGER;  // reads a log
     constexpr bool TOKEN = MODE != MODE_FOLD;    // decodes a token
-    constexpr bool WRITES = MODE != MODE_APPEND; // writes a dense state
-    constexpr bool CUR_IN_LOG = MODE == MODE_MERGE && DELTA;  // fold the token as entry L
+    constexpr bool AUTO = MODE == MODE_AUTO;     // append or fold, per slot, at run time
+    constexpr bool CAN_WRITE = MODE != MODE_APPEND;  // may write a dense state
     constexpr int CP = LOGGED ? CMAX : 4;        // entry slots in LDS (multiple of 4)
     constexpr int KPASS = LOGGED ? (CMAX + EPP - 1) / EPP : 1;
     constexpr int XR = LOGGED ? (CMAX + RPP - 1) / RPP : 1;  // log value rows per thread
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     __shared__ __attribute__((aligned(16))) float s_krow[D];   // current key, per row
     __shared__ __attribute__((aligned(16))) float s_wrow[D];   // RWKV6: current decay, per row
     __shared__ __attribute__((aligned(16))) float s_kt[LOGGED ? CP * D : 4];  // [entry][row] decayed keys
-    __shared__ __attribute__((aligned(16))) float s_x[LOGGED && WRITES ? CP * TV : 4];  // [entry][tile col]
+    __shared__ __attribute__((aligned(16))) float s_x[LOGGED && CAN_WRITE ? CP * TV : 4];  // [entry][tile col]
     __shared__ float s_coef[2][CP];  // replay coefficients: k side, q/r side
     __shared__ __attribute__((aligned(16))) float s_red[NW][2][TV];
     __shared__ __attribute__((aligned(16))) float s_u[TV];  // current value factor
@@ -209,6 +209,12 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         if (MODE == MODE_APPEND && L + 1 == C) return;
         if (MODE == MODE_MERGE && L + 1 != C) return;
     }
+    // What this workgroup does (uniform across it): compile-time except in
+    // AUTO mode, where the token that fills the log also folds it.
+    const bool fold = AUTO ? (L + 1 == C) : MODE == MODE_MERGE;
+    const bool append = AUTO ? !fold : MODE == MODE_APPEND;
+    const bool writes = AUTO ? fold : CAN_WRITE;  // writes a dense state
+    const bool cur_in_log = fold && DELTA;        // fold the token as entry L
     const int last = L > 0 ? L - 1 : 0;  // newest log entry (clamp target of masked loads)
     const int cg = tid % LPR;            // float4 column group: tile columns 4cg .. 4cg+3
     const int rs = tid / LPR;            // rows rs + RPP*i, i < R
@@ -309,15 +315,15 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         *reinterpret_cast<f4 *>(&s_scale[c4]) = sc;
         *reinterpret_cast<f4 *>(&s_krow[c4]) = k;
         *reinterpret_cast<f4 *>(&s_wrow[c4]) = dv;
-        if (LOGGED && CUR_IN_LOG) *reinterpret_cast<f4 *>(&s_kt[L * D + c4]) = k;
+        if (LOGGED && CAN_WRITE && cur_in_log) *reinterpret_cast<f4 *>(&s_kt[L * D + c4]) = k;
     }
     // append the token's key side as entry L (one writer per value; tile 0)
-    if (MODE == MODE_APPEND && tile == 0 && ke == 0) {
+    if (append && tile == 0 && ke == 0) {
         const size_t e = (size_t)n * C + L;
         *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * D + c4) = kraw;
         if (!GDN) *reinterpret_cast<f4 *>(p.logG + e * D + c4) = gn;
     }
-    if (MODE == MODE_APPEND && GDN && tile == 0 && tid == 0) p.logG[(size_t)n * C + L] = gn.x;
+    if (append && GDN && tile == 0 && tid == 0) p.logG[(size_t)n * C + L] = gn.x;
     if (TOKEN) {
         // every key-side group holds all D channels, so each group's sum is complete
         float part = DELTA ? dot4(k, q) : dot4(q * bon4, k);
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             if (!valid) kt = f4{0.f, 0.f, 0.f, 0.f};
             pk[ps] = dot4(kt, k);
             pq[ps] = dot4(kt, q);
-            if (WRITES && valid) *reinterpret_cast<f4 *>(&s_kt[i * D + c4]) = kt;
+            if (CAN_WRITE && writes && valid) *reinterpret_cast<f4 *>(&s_kt[i * D + c4]) = kt;
         }
         if (TOKEN) {
 #pragma unroll
@@ -363,7 +369,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             }
         }
         // value side of the log for the fold: this tile's columns of entries 0..L-1
-        if (WRITES) {
+        if (CAN_WRITE && writes) {
 #pragma unroll
             for (int j = 0; j < XR; ++j) {
                 const int i = rs + RPP * j;
@@ -371,8 +377,8 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             }
         }
         // zero the slots between the last folded entry and the next multiple of four
-        if (WRITES) {
-            const int ne = CUR_IN_LOG ? L + 1 : L;
+        if (CAN_WRITE && writes) {
+            const int ne = cur_in_log ? L + 1 : L;
             const int pad = ((ne + 3) & ~3) - ne;
             for (int idx = tid; idx < pad * D; idx += NT) {
                 const int i = ne + idx / D;
@@ -445,26 +451,26 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
                 o = zj + s_dot * vj;
             }
             p.out[(size_t)n * D + j] = o;
-            if (MODE == MODE_APPEND) {
+            if (append) {
                 const size_t e = (size_t)n * C + L;
                 if (DELTA)
                     static_cast<float *>(p.logX)[e * D + j] = xnew;
                 else
                     static_cast<TIn *>(p.logX)[e * D + j] = vraw;
             }
-            if (LOGGED && CUR_IN_LOG)
+            if (LOGGED && CAN_WRITE && cur_in_log)
                 s_x[L * TV + jt] = xnew;
             else
                 s_u[jt] = xnew;
         }
-        if (WRITES) __syncthreads();
+        if (CAN_WRITE && writes) __syncthreads();
     }
 
-    if (WRITES) {
+    if (CAN_WRITE && writes) {
         // ---------------- Phase E: write the state ----------------
         // row scale, the rank-(entries) update from LDS, then the current
         // token for RWKV6 and the eager form.
-        const int ne = CUR_IN_LOG ? L + 1 : L;
+        const int ne = cur_in_log ? L + 1 : L;
         f4 acc[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rs + RPP * i];
@@ -482,12 +488,12 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
                 }
             }
         }
-        if (TOKEN && !CUR_IN_LOG) {
+        if (TOKEN && !cur_in_log) {
             const f4 u = *reinterpret_cast<const f4 *>(&s_u[4 * cg]);
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 const int row = rs + RPP * i;
-                if (MODE == MODE_MERGE)  // RWKV6: decay the logical state, then add k v^T
+                if (fold)  // RWKV6: decay the logical state, then add k v^T
                     acc[i] = acc[i] * s_wrow[row] + s_krow[row] * u;
                 else
                     acc[i] += s_krow[row] * u;
@@ -520,6 +526,9 @@ hipError_t launch_mode(int mode, int cmax, const StepParams &p, hipStream_t s) {
         case MODE_FOLD:
             return small ? launch_one<OP, TIn, D, MODE_FOLD, 8>(p, s)
                          : launch_one<OP, TIn, D, MODE_FOLD, 32>(p, s);
+        case MODE_AUTO:
+            return small ? launch_one<OP, TIn, D, MODE_AUTO, 8>(p, s)
+                         : launch_one<OP, TIn, D, MODE_AUTO, 32>(p, s);
         case MODE_EAGER:
             return launch_one<OP, TIn, D, MODE_EAGER, 4>(p, s);
         default:

@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-eager", action="store_true", help="skip the eager GPU kernel")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the CPU-baseline sample")
     ap.add_argument("--report", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="also time multi-token decode: K tokens per dl_decode_tokens call")
     ap.add_argument("--staggered", action="store_true",
                     help="also time per-slot logs with slot b starting at token b mod C, so that "
                          "1/C of the slots fold at every step (continuous batching)")
@@ -291,6 +293,10 @@ def main():
                            "model_MB_per_token": round(eb / 1e6, 2)}
         result["speedup_vs_eager"] = round(e_wall_us / us_per_token, 3)
 
+    if args.tokens > 0:
+        result["multi_token"] = multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K,
+                                                  args.tokens)
+
     if args.staggered and C > 1:
         result["staggered"] = staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K)
 
@@ -314,6 +320,55 @@ def main():
     if args.report:
         with open(args.report, "a") as f:
             f.write(line + "\n")
+
+
+def multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K, ntok):
+    """K cycles of C tokens decoded ntok at a time with dl_decode_tokens."""
+    import ctypes
+    import torch
+    base = d["S0"].clone()
+    st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
+    T = w.T
+    one = [st.step_args(d["q"][t], d["k"][t], d["v"][t], None if d["beta"] is None else d["beta"][t],
+                        d["decay"][t], d["bonus"], outs[t]) for t in range(T)]
+    fn = dl.load_library().dl_decode_tokens
+    sptr = stream.cuda_stream
+    # the call sequence of one cycle: chunk sizes as the library splits them at C
+    calls, left, L = [], C, 0
+    while left > 0:
+        k = min(ntok, C - L)
+        calls.append(k)
+        L = 0 if L + k == C else L + k
+        left -= k
+    # every call's argument array is built before the timed region
+    ntot = 3 + K
+    schedule, tok = [], 0
+    for _ in range(ntot):
+        for k in calls:
+            schedule.append((k, (dl.StepArgs * k)(*[one[(tok + i) % T] for i in range(k)])))
+            tok += k
+    warm = 3 * len(calls)
+
+    def run(lo, hi):
+        for k, arr in schedule[lo:hi]:
+            assert fn(st.handle, arr, k, sptr) == 0
+
+    run(0, warm)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    run(warm, len(schedule))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) * 1e6 / (K * C)
+    st.close()
+    cyc = traffic.multi_token_cycle_bytes(sh, C, ntok)
+    return {"tokens_per_call": ntok, "us_per_token": round(wall_us, 3),
+            "events_us_per_token": round(e0.elapsed_time(e1) * 1e3 / (K * C), 3),
+            "model_MB_per_token": round(cyc / C / 1e6, 2),
+            "achieved_GBps": round(cyc / C / (wall_us * 1e-6) / 1e9, 1)}
 
 
 def staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K):

@@ -59,6 +59,7 @@ extern "C" {
 #endif
 
 #define DL_MAX_CAPACITY 32
+#define DL_MAX_TOKENS 8
 
 typedef enum { DL_GDN = 0, DL_KDA = 1, DL_RWKV6 = 2 } dl_op;
 typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
@@ -127,6 +128,18 @@ dl_status dl_state_init(dl_state **out, const dl_config *cfg, float *base,
  * launch also folds all C factors into the base with one read and one write
  * of the base (L becomes 0).  With C == 1 every step is the eager update. */
 dl_status dl_decode_step(dl_state *h, const dl_step_args *args, void *stream);
+
+/* Decode K consecutive tokens of every head (1 <= K <= DL_MAX_TOKENS):
+ * args[0..K-1] are the tokens in order, each as for dl_decode_step, and
+ * args[t].out receives o_t.  The tokens share one read of the base: the log
+ * grows by the chunk, and a chunk that fills the log folds it (a chunk that
+ * would pass C is split there, one launch per part).  The result equals K
+ * calls of dl_decode_step.  Lockstep handles only (DL_ERR_UNSUPPORTED on a
+ * per-slot handle).  This is the multi-token neighbour of single-token
+ * decode (drafted tokens to verify, short continuations); it follows from
+ * the same base-plus-log representation (gist.science summary, "Meccanismo
+ * Core: Base + Log"). */
+dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *stream);
 
 /* Fold the current log into the base now (an early merge), L becomes 0.
  * Output-neutral: later outputs are unchanged.  A no-op when L == 0. */

@@ -18,6 +18,7 @@ DL_F32, DL_BF16 = 0, 1
 DL_OK = 0
 DL_ERR_ARG, DL_ERR_SHAPE, DL_ERR_UNSUPPORTED, DL_ERR_HIP, DL_ERR_WORKSPACE = -1, -2, -3, -4, -5
 DL_MAX_CAPACITY = 32
+DL_MAX_TOKENS = 8
 
 OP_CODES = {"gdn": DL_GDN, "kda": DL_KDA, "rwkv6": DL_RWKV6}
 DTYPE_CODES = {"f32": DL_F32, "bf16": DL_BF16}
@@ -67,6 +68,7 @@ def load_library():
         "dl_workspace_layout": (i, [cp, ctypes.POINTER(sz)]),
         "dl_state_init": (i, [ctypes.POINTER(vp), cp, vp, vp, sz]),
         "dl_decode_step": (i, [vp, ap, vp]),
+        "dl_decode_tokens": (i, [vp, ap, i, vp]),
         "dl_merge": (i, [vp, vp]),
         "dl_materialize": (i, [vp, vp, vp]),
         "dl_log_length": (i, [vp]),
@@ -141,6 +143,12 @@ def dl_slot_log_length(handle, slot):
 
 def dl_decode_step(handle, args, stream=0):
     _check(load_library().dl_decode_step(handle, ctypes.byref(args), stream))
+
+
+def dl_decode_tokens(handle, args_list, stream=0):
+    """args_list: a sequence of StepArgs, the tokens in order."""
+    arr = (StepArgs * len(args_list))(*args_list)
+    _check(load_library().dl_decode_tokens(handle, arr, len(args_list), stream))
 
 
 def dl_merge(handle, stream=0):

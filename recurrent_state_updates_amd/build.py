@@ -18,7 +18,8 @@ LIB = os.path.join(PKG, "libdeltalog.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["deltalog.cpp", "kernels_gdn.hip", "kernels_kda.hip", "kernels_rwkv6.hip", "slots.hip"]
+SOURCES = ["deltalog.cpp", "kernels_gdn.hip", "kernels_kda.hip", "kernels_rwkv6.hip", "slots.hip",
+           "kernels_gdn_chunk.hip", "kernels_kda_chunk.hip", "kernels_rwkv6_chunk.hip"]
 
 # Packed fp32 VALU ops are switched off for all device code; the host pass
 # prints that it does not know the feature, which is harmless.

@@ -1,0 +1,382 @@
+// chunk_kernel.h -- decode K consecutive tokens of every head in one launch.
+//
+// The single-token step reads the whole base once per token.  When several
+// tokens of the same heads are available at once (a draft chain to verify,
+// a short prompt continuation), they can share that read: with the base held
+// in registers the workgroup forms every token's base products, replays the
+// log for each, and resolves the dependence of token t on the earlier tokens
+// of the chunk by a forward substitution over the value factors, column by
+// column.  The tokens are then appended to the log, or, when the chunk fills
+// it, the whole log is folded into the base with one read and one write.
+//
+// Algebra (per head; g_t = g_L + sum_{m<=t} log2 decay_m, g_{-1} = g_L; the
+// reference point rho_t = g_t for the delta rules, g_{t-1} for RWKV6):
+//   base products  Y0_t = Sbar^T (2^{rho_t} k_t) + sum_{i<L} x_i <k_i 2^{rho_t-g_i}, k_t>
+//                  Z0_t = the same with q_t (or r_t)
+//   delta rules    u_t = beta_t (v_t - Y0_t - sum_{m<t} u_m <k_m 2^{g_t-g_m}, k_t>)
+//                  o_t = Z0_t + sum_{m<t} u_m <k_m 2^{g_t-g_m}, q_t> + <k_t, q_t> u_t
+//   RWKV6          o_t = Z0_t + sum_{m<t} v_m <k_m 2^{g_{t-1}-g_m}, r_t> + (sum_c r u k) v_t
+//   entries        (k_t, u_t or v_t, g_t); a fold writes
+//                  S = diag(2^{g_{K-1}}) Sbar + sum_e (k_e 2^{g_{K-1}-g_e}) x_e^T over all entries.
+#pragma once
+
+#include "step_kernel.h"
+
+namespace dlk {
+
+template <int OP, typename TIn, int D, int TV, int NT, int CMAX>
+__global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
+    using G = Geom<D, TV, NT>;
+    constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
+    constexpr int KL = G::KL, EPP = G::EPP;
+    constexpr bool GDN = OP == OP_GDN;
+    constexpr bool DELTA = OP != OP_RWKV6;
+    constexpr int KM = KMAX_TOKENS;
+    constexpr int CP = CMAX;  // entry slots: old entries plus the chunk's tokens (<= C <= CMAX)
+    constexpr int KPASS = (CMAX + EPP - 1) / EPP;
+    constexpr int XR = (CMAX + RPP - 1) / RPP;
+    constexpr int GW = GDN ? 1 : D;  // log-decay values per entry
+    using TX = typename std::conditional<DELTA, float, TIn>::type;
+    using Raw = typename In4<TIn>::raw;
+    using RawX = typename In4<TX>::raw;
+    static_assert(KM <= EPP, "one key-side group per token");
+    static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
+
+    __shared__ __attribute__((aligned(16))) float s_k[KM][D];      // token keys
+    __shared__ __attribute__((aligned(16))) float s_q[KM][D];      // token queries (receptances)
+    __shared__ __attribute__((aligned(16))) float s_lg[KM][GW];    // log2 of each token's decay
+    __shared__ __attribute__((aligned(16))) float s_g[KM + 1][GW]; // g_{t-1} at index t (g_{-1} = g_L)
+    __shared__ __attribute__((aligned(16))) float s_mv0[KM][D];    // 2^{rho_t} k_t
+    __shared__ __attribute__((aligned(16))) float s_mv1[KM][D];    // 2^{rho_t} q_t (r_t)
+    __shared__ __attribute__((aligned(16))) float s_scale[D];      // fold: 2^{g_{K-1}} per row
+    __shared__ __attribute__((aligned(16))) float s_kt[CP * D];    // fold: decayed keys [entry][row]
+    __shared__ __attribute__((aligned(16))) float s_x[CP * TV];    // fold: value factors [entry][col]
+    __shared__ float s_coef[2][KM][CP];                            // per token, per entry
+    __shared__ __attribute__((aligned(16))) float s_red[KM][NW][2][TV];
+    __shared__ float s_dot[KM];   // <k_t, q_t> or sum r u k
+    __shared__ float s_beta[KM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    int n, tile;
+    block_to_tile(blockIdx.x, p.N, NTILE, n, tile);
+    const int C = p.C;
+    const int L = p.L;
+    const int K = p.K;
+    const bool fold = p.fold != 0;
+    const int NE = L + K;               // entries after the chunk
+    const int last = L > 0 ? L - 1 : 0;
+    const int cg = tid % LPR;
+    const int rs = tid / LPR;
+    const int col0 = tile * TV;
+    const int c4 = 4 * (tid % KL);
+    const int ke = tid / KL;            // key-side group: token ke, then entries ps*EPP + ke
+
+    // ---------------- Phase A: loads (token ke's key side, the old log, the tile) ----------------
+    // token tk = min(ke, K-1): groups beyond the chunk load a valid token and ignore it
+    const int tk = min(ke, K - 1);
+    const Raw kraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.k[tk]) + (size_t)n * D + c4);
+    const Raw qraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.q[tk]) + (size_t)n * D + c4);
+    f4 dec4 = {1.f, 1.f, 1.f, 1.f};
+    float alpha = 1.f;
+    if (GDN)
+        alpha = p.decay[tk][n];
+    else
+        dec4 = *reinterpret_cast<const f4 *>(p.decay[tk] + (size_t)n * D + c4);
+    TIn vraw[KM];
+#pragma unroll
+    for (int t = 0; t < KM; ++t)
+        vraw[t] = t < K ? static_cast<const TIn *>(p.v[t])[(size_t)n * D + col0 + tid % TV] : TIn{};
+    float glast_s = 0.f;
+    f4 glast4 = {0.f, 0.f, 0.f, 0.f};
+    Raw klog[KPASS];
+    float glog_s[KPASS];
+    f4 glog4[KPASS];
+    RawX xrow[XR];
+    {
+        const size_t el = (size_t)n * C + last;
+        if (GDN)
+            glast_s = p.logG[el];
+        else
+            glast4 = *reinterpret_cast<const f4 *>(p.logG + el * D + c4);
+#pragma unroll
+        for (int ps = 0; ps < KPASS; ++ps) {
+            const size_t e = (size_t)n * C + min(ps * EPP + ke, last);
+            klog[ps] = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.logK) + e * D + c4);
+            if (GDN)
+                glog_s[ps] = p.logG[e];
+            else
+                glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * D + c4);
+        }
+        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0 + 4 * cg;
+#pragma unroll
+        for (int j = 0; j < XR; ++j)
+            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * D);
+    }
+    const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
+    const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
+    f4 s[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
+
+    // ---------------- Phase B1: every token's inputs into LDS (group ke = token) ----------------
+    const f4 kt_in = In4<TIn>::unpack(kraw);
+    const f4 qt_in = In4<TIn>::unpack(qraw);
+    if (ke < K) {
+        *reinterpret_cast<f4 *>(&s_k[ke][c4]) = kt_in;
+        *reinterpret_cast<f4 *>(&s_q[ke][c4]) = qt_in;
+        if (GDN) {
+            if (c4 == 0) s_lg[ke][0] = log2f(alpha);
+        } else {
+            *reinterpret_cast<f4 *>(&s_lg[ke][c4]) = log2v(dec4);
+        }
+        if (c4 == 0 && DELTA) s_beta[ke] = p.beta[ke][n];
+    }
+    if (ke == 0) {  // g_{-1} = g_L, newest old entry's cumulative log-decay
+        if (GDN) {
+            if (c4 == 0) s_g[0][0] = L > 0 ? glast_s : 0.f;
+        } else {
+            *reinterpret_cast<f4 *>(&s_g[0][c4]) = L > 0 ? glast4 : f4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+    __syncthreads();
+    // prefix sums of the log-decays: g_t for every token (group 0, four channels per thread)
+    if (ke == 0) {
+        if (GDN) {
+            if (c4 == 0) {
+                float g = s_g[0][0];
+                for (int t = 0; t < K; ++t) {
+                    g += s_lg[t][0];
+                    s_g[t + 1][0] = g;
+                }
+            }
+        } else {
+            f4 g = *reinterpret_cast<const f4 *>(&s_g[0][c4]);
+            for (int t = 0; t < K; ++t) {
+                g += *reinterpret_cast<const f4 *>(&s_lg[t][c4]);
+                *reinterpret_cast<f4 *>(&s_g[t + 1][c4]) = g;
+            }
+        }
+    }
+    __syncthreads();
+
+    auto g_at = [&](int idx) -> f4 {  // g_{idx-1} for the thread's four channels
+        if (GDN) {
+            const float g = s_g[idx][0];
+            return f4{g, g, g, g};
+        }
+        return *reinterpret_cast<const f4 *>(&s_g[idx][c4]);
+    };
+
+    // ---------------- Phase B2: per token: scaled key / query, dot, log append ----------------
+    if (ke < K) {
+        const int t = ke;
+        const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
+        const f4 sc = exp2v(rho);
+        *reinterpret_cast<f4 *>(&s_mv0[t][c4]) = sc * kt_in;
+        *reinterpret_cast<f4 *>(&s_mv1[t][c4]) = sc * qt_in;
+        float part;
+        if (DELTA) {
+            part = dot4(kt_in, qt_in);
+        } else {
+            const f4 bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
+            part = dot4(qt_in * bon4, kt_in);
+        }
+        part = group_sum<KL>(part);
+        if (c4 == 0) s_dot[t] = part;
+        if (!fold && tile == 0) {  // entry L + t of the log: the key copy and its log-decay
+            const size_t e = (size_t)n * C + L + t;
+            *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * D + c4) = kraw;
+            if (GDN) {
+                if (c4 == 0) p.logG[e] = g_at(t + 1).x;
+            } else {
+                *reinterpret_cast<f4 *>(p.logG + e * D + c4) = g_at(t + 1);
+            }
+        }
+    }
+    if (fold && ke == 0) *reinterpret_cast<f4 *>(&s_scale[c4]) = exp2v(g_at(K));
+
+    // ---------------- Phase B3: coefficients of every (token, entry) pair ----------------
+    const f4 gend = g_at(K);  // g_{K-1}: the fold's decay point
+#pragma unroll
+    for (int ps = 0; ps < KPASS; ++ps) {
+        const int e = ps * EPP + ke;
+        const bool is_old = e < L;
+        const bool is_new = e >= L && e < NE;
+        f4 ke4, ge4;
+        if (is_old) {
+            ke4 = In4<TIn>::unpack(klog[ps]);
+            ge4 = GDN ? f4{glog_s[ps], glog_s[ps], glog_s[ps], glog_s[ps]} : glog4[ps];
+        } else if (is_new) {
+            ke4 = *reinterpret_cast<const f4 *>(&s_k[e - L][c4]);
+            ge4 = g_at(e - L + 1);
+        } else {
+            ke4 = f4{0.f, 0.f, 0.f, 0.f};
+            ge4 = f4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int t = 0; t < K; ++t) {
+            const bool valid = is_old || (is_new && e - L < t);
+            const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
+            f4 kt = valid ? ke4 * exp2v(rho - ge4) : f4{0.f, 0.f, 0.f, 0.f};
+            float pk = dot4(kt, *reinterpret_cast<const f4 *>(&s_k[t][c4]));
+            float pq = dot4(kt, *reinterpret_cast<const f4 *>(&s_q[t][c4]));
+            pk = group_sum<KL>(pk);
+            pq = group_sum<KL>(pq);
+            if (c4 == 0 && e < NE) {
+                s_coef[0][t][e] = valid ? pk : 0.f;
+                s_coef[1][t][e] = valid ? pq : 0.f;
+            }
+        }
+        if (fold && (is_old || is_new))
+            *reinterpret_cast<f4 *>(&s_kt[e * D + c4]) = ke4 * exp2v(gend - ge4);
+    }
+    if (fold) {
+        // old value factors of the tile for the fold; zero the slots up to a multiple of four
+#pragma unroll
+        for (int j = 0; j < XR; ++j) {
+            const int i = rs + RPP * j;
+            if (i < L) *reinterpret_cast<f4 *>(&s_x[i * TV + 4 * cg]) = In4<TX>::unpack(xrow[j]);
+        }
+        const int pad = ((NE + 3) & ~3) - NE;
+        for (int idx = tid; idx < pad * D; idx += NT) {
+            const int i = NE + idx / D;
+            const int c = idx % D;
+            s_kt[i * D + c] = 0.f;
+            if (c < TV) s_x[i * TV + c] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- Phase C: base products of every token from the register tile ----------------
+    for (int t = 0; t < K; ++t) {
+        f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int row = rs + RPP * i;
+            if (DELTA) y += s[i] * s_mv0[t][row];
+            z += s[i] * s_mv1[t][row];
+        }
+#pragma unroll
+        for (int j = 0; j < XR; ++j) {
+            const int i = rs + RPP * j;
+            if (i < L) {
+                const f4 x = In4<TX>::unpack(xrow[j]);
+                if (DELTA) y += s_coef[0][t][i] * x;
+                z += s_coef[1][t][i] * x;
+            }
+        }
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) {
+            if (DELTA) {
+                y.x += __shfl_xor(y.x, off);
+                y.y += __shfl_xor(y.y, off);
+                y.z += __shfl_xor(y.z, off);
+                y.w += __shfl_xor(y.w, off);
+            }
+            z.x += __shfl_xor(z.x, off);
+            z.y += __shfl_xor(z.y, off);
+            z.z += __shfl_xor(z.z, off);
+            z.w += __shfl_xor(z.w, off);
+        }
+        if (lane < LPR) {
+            if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][wave][0][4 * cg]) = y;
+            *reinterpret_cast<f4 *>(&s_red[t][wave][1][4 * cg]) = z;
+        }
+    }
+    __syncthreads();
+
+    // ---------------- Phase D: per column, the chunk's tokens in order ----------------
+    if (tid < TV) {
+        const int jt = tid;
+        const int j = col0 + jt;
+        float xs[KM];  // value factors of the chunk's tokens in this column
+#pragma unroll
+        for (int t = 0; t < KM; ++t) {
+            if (t >= K) break;
+            float yj = 0.f, zj = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                if (DELTA) yj += s_red[t][w][0][jt];
+                zj += s_red[t][w][1][jt];
+            }
+#pragma unroll
+            for (int m = 0; m < KM; ++m) {
+                if (m >= t) break;
+                if (DELTA) yj += s_coef[0][t][L + m] * xs[m];
+                zj += s_coef[1][t][L + m] * xs[m];
+            }
+            const float vj = to_f32(vraw[t]);
+            float xnew, o;
+            if (DELTA) {
+                xnew = s_beta[t] * (vj - yj);
+                o = zj + s_dot[t] * xnew;
+            } else {
+                xnew = vj;
+                o = zj + s_dot[t] * vj;
+            }
+            xs[t] = xnew;
+            p.out[t][(size_t)n * D + j] = o;
+            if (fold) {
+                s_x[(L + t) * TV + jt] = xnew;
+            } else {
+                const size_t e = (size_t)n * C + L + t;
+                if (DELTA)
+                    static_cast<float *>(p.logX)[e * D + j] = xnew;
+                else
+                    static_cast<TIn *>(p.logX)[e * D + j] = vraw[t];
+            }
+        }
+    }
+
+    // ---------------- Phase E: fold every entry into the base when the chunk fills the log ----------------
+    if (fold) {
+        __syncthreads();
+        f4 acc[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rs + RPP * i];
+        for (int e = 0; e < NE; e += 4) {
+            const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + 4 * cg]);
+            const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + 4 * cg]);
+            const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + 4 * cg]);
+            const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + 4 * cg]);
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const int row = rs + RPP * i;
+                acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
+                          s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
+            }
+        }
+        f4 *dst4 = reinterpret_cast<f4 *>(p.base) + tile4;
+#pragma unroll
+        for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RPP * (D / 4));
+    }
+}
+
+template <int OP, typename TIn, int D, int CMAX>
+hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
+    constexpr int TV = Shape<D>::TV, NT = Shape<D>::NT;
+    const unsigned blocks = (unsigned)p.N * (D / TV);
+    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX>), dim3(blocks), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int OP, typename TIn>
+hipError_t launch_chunk_width(int D, int cmax, const ChunkParams &p, hipStream_t s) {
+    const bool small = cmax <= 8;
+    switch (D) {
+        case 32: return small ? launch_chunk_one<OP, TIn, 32, 8>(p, s) : launch_chunk_one<OP, TIn, 32, 32>(p, s);
+        case 64: return small ? launch_chunk_one<OP, TIn, 64, 8>(p, s) : launch_chunk_one<OP, TIn, 64, 32>(p, s);
+        case 128:
+            return small ? launch_chunk_one<OP, TIn, 128, 8>(p, s) : launch_chunk_one<OP, TIn, 128, 32>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OP>
+hipError_t launch_chunk_op(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s) {
+    return in_bf16 ? launch_chunk_width<OP, bf16_bits>(D, cmax, p, s)
+                   : launch_chunk_width<OP, float>(D, cmax, p, s);
+}
+
+}  // namespace dlk

@@ -13,6 +13,7 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <limits>
 #include <new>
 #include <string>
@@ -313,6 +314,56 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
     st = launch(&h->cfg, fold ? dlk::MODE_MERGE : dlk::MODE_APPEND, p, stream);
     if (st != DL_OK) return st;
     h->L = fold ? 0 : h->L + 1;
+    return DL_OK;
+}
+
+dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *stream) {
+    if (!h) return fail(DL_ERR_ARG, "handle is NULL");
+    size_t heads = 0;
+    dl_status st = check_config(&h->cfg, &heads);
+    if (st != DL_OK) return st;
+    if (h->slots) return fail(DL_ERR_UNSUPPORTED, "multi-token decode needs a lockstep handle");
+    if (!args) return fail(DL_ERR_ARG, "args is NULL");
+    if (K < 1 || K > DL_MAX_TOKENS) return fail(DL_ERR_SHAPE, "K must lie in [1, 8]");
+    for (int t = 0; t < K; ++t)
+        if ((st = check_args(&h->cfg, &args[t])) != DL_OK) return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int cmax = h->cfg.C <= 8 ? 8 : 32;
+    const int bf16 = h->cfg.in_dtype == DL_BF16;
+    for (int t0 = 0; t0 < K;) {
+        const int k1 = std::min(K - t0, h->cfg.C - h->L);  // the part that fits the log
+        dlk::ChunkParams p = {};
+        p.base = h->base;
+        for (int t = 0; t < k1; ++t) {
+            const dl_step_args &a = args[t0 + t];
+            p.q[t] = a.q;
+            p.k[t] = a.k;
+            p.v[t] = a.v;
+            p.beta[t] = a.beta;
+            p.decay[t] = a.decay;
+            p.out[t] = a.out;
+        }
+        p.bonus = args[t0].bonus;
+        p.logX = h->logX;
+        p.logK = h->logK;
+        p.logG = h->logG;
+        p.L = h->L;
+        p.C = h->cfg.C;
+        p.H = h->cfg.H;
+        p.N = (int)heads;
+        p.K = k1;
+        p.fold = h->L + k1 == h->cfg.C;
+        hipError_t e;
+        switch (h->cfg.op) {
+            case DL_GDN: e = dlk::launch_gdn_chunk(bf16, h->cfg.dk, cmax, p, s); break;
+            case DL_KDA: e = dlk::launch_kda_chunk(bf16, h->cfg.dk, cmax, p, s); break;
+            default: e = dlk::launch_rwkv6_chunk(bf16, h->cfg.dk, cmax, p, s); break;
+        }
+        if (e != hipSuccess)
+            return fail(DL_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        h->L = p.fold ? 0 : h->L + k1;
+        t0 += k1;
+    }
     return DL_OK;
 }
 

@@ -46,6 +46,32 @@ hipError_t launch_gdn(int in_bf16, int D, int mode, int cmax, const StepParams &
 hipError_t launch_kda(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
 hipError_t launch_rwkv6(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
 
+// Several consecutive tokens of every head in one launch (lockstep log).
+constexpr int KMAX_TOKENS = 8;
+struct ChunkParams {
+    float *base;                        // [N][D][D] fp32, rewritten in place when fold
+    const void *q[KMAX_TOKENS];         // token t: [N][D] input dtype
+    const void *k[KMAX_TOKENS];
+    const void *v[KMAX_TOKENS];
+    const float *beta[KMAX_TOKENS];     // [N] (GDN, KDA)
+    const float *decay[KMAX_TOKENS];    // [N] (GDN) or [N][D]
+    float *out[KMAX_TOKENS];            // [N][D] fp32
+    const float *bonus;                 // [H][D] (RWKV6)
+    void *logX;
+    void *logK;
+    float *logG;
+    int L;     // log entries before the chunk
+    int C;     // capacity; L + K <= C
+    int H;
+    int N;
+    int K;     // tokens in the chunk, 1 <= K <= KMAX_TOKENS
+    int fold;  // 1: L + K == C, fold every entry into the base
+};
+
+hipError_t launch_gdn_chunk(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s);
+hipError_t launch_kda_chunk(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s);
+hipError_t launch_rwkv6_chunk(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s);
+
 // Set slot_base / slot_active entries: slot < 0 means every slot (with
 // only_active, every active slot); set_base / set_active select the fields.
 hipError_t launch_slot_set(int *slot_base, unsigned char *slot_active, int B, int slot, int set_base,

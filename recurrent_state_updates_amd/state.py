@@ -96,6 +96,18 @@ class DeltaLogState:
         B.dl_decode_step(self.handle, args, _stream(self.device))
         return out
 
+    def step_tokens(self, q, k, v, beta, decay, bonus=None, out=None):
+        """Decode K tokens in one call (dl_decode_tokens).  q, k, v, beta, decay
+        carry a leading token axis [K, ...]; returns out [K, B, H, dv] fp32."""
+        K = q.shape[0]
+        if out is None:
+            out = torch.empty((K, self.B, self.H, self.dv), dtype=torch.float32, device=self.device)
+        args = [make_step_args(self.op, self.in_dtype, self.B, self.H, self.dk, self.dv, self.device,
+                               q[t], k[t], v[t], None if beta is None else beta[t], decay[t], bonus, out[t])
+                for t in range(K)]
+        B.dl_decode_tokens(self.handle, args, _stream(self.device))
+        return out
+
     def step_args(self, q, k, v, beta, decay, bonus, out):
         """Pre-validated StepArgs for repeated low-overhead ``step_packed`` calls."""
         return make_step_args(self.op, self.in_dtype, self.B, self.H, self.dk, self.dv,

@@ -75,6 +75,29 @@ def eager_bytes(sh: Shape) -> int:
     return sh.heads * per + sh.shared()
 
 
+def chunk_bytes(sh: Shape, L: int, K: int, fold: bool) -> int:
+    """K tokens in one launch at log length L: one base read (and write when
+    the chunk fills the log), K tokens in and out, L entries replayed, and the
+    K new entries written unless they are folded."""
+    per = sh.base() * (2 if fold else 1) + K * (sh.token_in() + sh.out()) + L * sh.entry()
+    if not fold:
+        per += K * sh.entry()
+    return sh.heads * per + sh.shared()
+
+
+def multi_token_cycle_bytes(sh: Shape, C: int, K: int) -> int:
+    """One merge cycle of C tokens decoded K at a time (chunks split at C)."""
+    total, L = 0, 0
+    left = C
+    while left > 0:
+        k = min(K, C - L)
+        fold = L + k == C
+        total += chunk_bytes(sh, L, k, fold)
+        L = 0 if fold else L + k
+        left -= k
+    return total
+
+
 def fold_bytes(sh: Shape, L: int) -> int:
     """A standalone fold (merge or materialise) of L entries."""
     return sh.heads * (2 * sh.base() + L * sh.entry())

@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), f"{name} is declared in deltalog.h but not exported"
     for name in names:
@@ -149,6 +149,23 @@ def test_decode_step_rejects_bad_args_without_state_change(op, over):
         dl.dl_state_destroy(h)
     lib = B.load_library()
     assert lib.dl_decode_step(None, ctypes.byref(_args()), None) == B.DL_ERR_ARG
+
+
+def test_decode_tokens_validates_before_launching():
+    cfg = dl.make_config("kda", "bf16", 2, 4, 64, 64, 4)
+    lib = B.load_library()
+    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    try:
+        for K in (0, 9):
+            arr = (B.StepArgs * max(K, 1))(*([_args()] * max(K, 1)))
+            assert lib.dl_decode_tokens(h, arr, K, None) == B.DL_ERR_SHAPE
+        assert lib.dl_decode_tokens(h, None, 2, None) == B.DL_ERR_ARG
+        with pytest.raises(dl.DeltaLogError) as ei:
+            dl.dl_decode_tokens(h, [_args(), _args(), _args(k=0)])  # the third token is bad
+        assert ei.value.status == B.DL_ERR_ARG
+        assert dl.dl_log_length(h) == 0
+    finally:
+        dl.dl_state_destroy(h)
 
 
 def test_slot_calls_validate_on_the_host():

@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--staggered", action="store_true",
                     help="also time per-slot logs with slot b starting at token b mod C, so that "
                          "1/C of the slots fold at every step (continuous batching)")
+    ap.add_argument("--split-ablation", action="store_true",
+                    help="also time the fused and the split replay preparation, each launched call by "
+                         "call and replayed as a captured merge-cycle graph")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 268 MB device-to-device copy (the reference kernel "
                          "for scaling hardware byte counters)")
@@ -297,6 +300,9 @@ def main():
         result["multi_token"] = multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K,
                                                   args.tokens)
 
+    if args.split_ablation and C > 1:
+        result["split_replay_ablation"] = split_ablation(dl, d, w, Bsz, C, dev, stream, outs, K)
+
     if args.staggered and C > 1:
         result["staggered"] = staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K)
 
@@ -369,6 +375,61 @@ def multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K, ntok)
             "events_us_per_token": round(e0.elapsed_time(e1) * 1e3 / (K * C), 3),
             "model_MB_per_token": round(cyc / C / 1e6, 2),
             "achieved_GBps": round(cyc / C / (wall_us * 1e-6) / 1e9, 1)}
+
+
+def split_ablation(dl, d, w, Bsz, C, dev, stream, outs, K):
+    """Amortised time per token over K merge cycles for the fused and the split
+    replay preparation, launched call by call and replayed from one captured
+    cycle.  The graph replays decode the same C tokens again (the work per
+    replay does not depend on the values), so no refill runs in the region."""
+    import ctypes
+    import torch
+    T = w.T
+    fn = dl.load_library().dl_decode_step
+    sptr = stream.cuda_stream
+    res = {}
+
+    def timed(body, ncyc):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        body(ncyc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e6 / (ncyc * C)
+        return {"us_per_token": round(wall, 3),
+                "events_us_per_token": round(e0.elapsed_time(e1) * 1e3 / (ncyc * C), 3)}
+
+    for split in (False, True):
+        name = "split" if split else "fused"
+        base = d["S0"].clone()
+        st = dl.DeltaLogState(w.op, w.in_dtype, base, C, split_replay=split)
+        refs = [ctypes.byref(st.step_args(d["q"][t], d["k"][t], d["v"][t],
+                                          None if d["beta"] is None else d["beta"][t], d["decay"][t],
+                                          d["bonus"], outs[t])) for t in range(T)]
+
+        def calls(ncyc):
+            for i in range(ncyc * C):
+                assert fn(st.handle, refs[i % T], sptr) == 0
+
+        calls(3)
+        res[f"{name}_launches"] = timed(calls, K)
+        tokens = [dict(q=d["q"][t], k=d["k"][t], v=d["v"][t],
+                       beta=None if d["beta"] is None else d["beta"][t], decay=d["decay"][t],
+                       bonus=d["bonus"], out=outs[t]) for t in range(C)]
+        graph = st.capture_cycle(tokens)
+
+        def replays(ncyc):
+            for _ in range(ncyc):
+                graph.launch(sptr)
+
+        replays(3)
+        res[f"{name}_graph"] = timed(replays, K)
+        graph.close()
+        st.close()
+    return res
 
 
 def staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K):

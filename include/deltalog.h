@@ -153,6 +153,54 @@ dl_status dl_materialize(const dl_state *h, float *dst, void *stream);
  * per-slot handle (see dl_slot_log_length). */
 int dl_log_length(const dl_state *h);
 
+/* Split replay (the pages' staged kernel: gist.science summary, "Implementazione
+ * del Kernel" -- a shared ReplayPrep stage computes the replay coefficients
+ * once per slot-head, then parallel AppendDecode stages run the value tiles;
+ * ablated against graph replay in the signal-papers summary, Fig. 9).
+ *
+ * By default every value-tile workgroup of an append recomputes the key-side
+ * preparation itself while its base tile is in flight (fused).  With a prep
+ * buffer set, each append instead runs two launches: one workgroup per head
+ * computes the scaled key and query (receptance), the replay coefficients
+ * and the token's scalar term into a per-head record and appends the key
+ * side of the entry; then the tile workgroups read that record.  The fold
+ * step (L + 1 == C) and dl_decode_tokens keep their fused form.  Results
+ * equal the fused path up to fp32 rounding.
+ *
+ * dl_prep_bytes: bytes of that buffer for cfg (N records of 2*dk + 2*M + 4
+ * fp32, M = 8 for C <= 8 and 32 otherwise); 0 for an invalid cfg.
+ * dl_set_split_replay: prep = device memory of at least dl_prep_bytes bytes,
+ * 16-byte aligned, owned by the caller and outliving its use (it holds no
+ * state between steps), or NULL to return to the fused form.  Lockstep
+ * handles only (DL_ERR_UNSUPPORTED on a per-slot handle); DL_ERR_WORKSPACE
+ * for a short buffer.  Host-only: enqueues nothing. */
+size_t dl_prep_bytes(const dl_config *cfg);
+dl_status dl_set_split_replay(dl_state *h, void *prep, size_t prep_bytes);
+
+/* Graph replay of one merge cycle (the pages time their kernels under graph
+ * replay: signal-papers summary, Fig. 9).
+ *
+ * dl_graph_capture_cycle records the C decode steps of one whole cycle --
+ * args[0..C-1], each as for dl_decode_step, in the handle's current mode
+ * (fused or split replay) -- into a HIP graph, without running them.  The
+ * log must be empty (dl_log_length() == 0, else DL_ERR_ARG); a whole cycle
+ * leaves it empty again, so the graph can be replayed any number of times.
+ * The graph keeps every pointer it was recorded with (inputs, outputs, base,
+ * workspace, prep): the caller refills the same input buffers before each
+ * replay.  Lockstep handles only (DL_ERR_UNSUPPORTED otherwise).  It creates
+ * and destroys a private capture stream and instantiates the graph, so
+ * unlike the other calls it asks the HIP runtime for resources.  *out
+ * receives the graph (NULL on error).
+ *
+ * dl_graph_launch enqueues one replay (C tokens) on `stream`; DL_ERR_ARG if
+ * the handle's log is not empty (a dl_decode_step since the last replay
+ * that did not complete a cycle).  dl_graph_destroy releases the graph (NULL
+ * is allowed); destroy it before its handle. */
+typedef struct dl_graph dl_graph; /* opaque, host memory only */
+dl_status dl_graph_capture_cycle(dl_graph **out, dl_state *h, const dl_step_args *args);
+dl_status dl_graph_launch(dl_graph *g, void *stream);
+void dl_graph_destroy(dl_graph *g);
+
 /* Per-slot logs (continuous batching).  The pages prepare replay
  * coefficients per slot-head (gist.science summary, "Implementazione del
  * Kernel") and serve many concurrent requests; here each of the B slots has

@@ -80,6 +80,11 @@ def load_library():
         "dl_slot_log_length": (i, [vp, i]),
         "dl_predict_token_us": (ctypes.c_double, [cp, ctypes.c_double, ctypes.c_double]),
         "dl_choose_capacity": (i, [cp, i, ctypes.c_double, ctypes.c_double]),
+        "dl_prep_bytes": (sz, [cp]),
+        "dl_set_split_replay": (i, [vp, vp, sz]),
+        "dl_graph_capture_cycle": (i, [ctypes.POINTER(vp), vp, ap]),
+        "dl_graph_launch": (i, [vp, vp]),
+        "dl_graph_destroy": (None, [vp]),
         "dl_status_string": (ctypes.c_char_p, [i]),
         "dl_last_error": (ctypes.c_char_p, []),
     }
@@ -179,6 +184,31 @@ def dl_choose_capacity(cfg, max_c=DL_MAX_CAPACITY, read_gbps=0.0, copy_gbps=0.0)
     if c < 0:
         _check(c)
     return c
+
+
+def dl_prep_bytes(cfg):
+    return int(load_library().dl_prep_bytes(ctypes.byref(cfg)))
+
+
+def dl_set_split_replay(handle, prep, prep_bytes):
+    """prep: device address of the record buffer, or 0 for the fused preparation."""
+    _check(load_library().dl_set_split_replay(handle, prep, prep_bytes))
+
+
+def dl_graph_capture_cycle(handle, args_list):
+    """Record one merge cycle (len(args_list) == C tokens); returns the graph (an integer)."""
+    arr = (StepArgs * len(args_list))(*args_list)
+    g = ctypes.c_void_p()
+    _check(load_library().dl_graph_capture_cycle(ctypes.byref(g), handle, arr))
+    return g.value
+
+
+def dl_graph_launch(graph, stream=0):
+    _check(load_library().dl_graph_launch(graph, stream))
+
+
+def dl_graph_destroy(graph):
+    load_library().dl_graph_destroy(graph)
 
 
 def dl_state_destroy(handle):

@@ -36,6 +36,14 @@ struct dl_state {
     std::vector<unsigned> h_base;
     std::vector<unsigned char> h_active;
     unsigned step;
+    // split replay: per-head prep records (NULL: the fused per-tile preparation)
+    float *prep;
+};
+
+// A merge cycle captured for replay (dl_graph_capture_cycle).
+struct dl_graph {
+    dl_state *h;
+    hipGraphExec_t exec;
 };
 
 namespace {
@@ -52,6 +60,9 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 size_t in_size(int dtype) { return dtype == DL_BF16 ? 2 : 4; }
+
+// Compile-time bound on log entries of the kernels that serve capacity C.
+int cmax_of(const dl_config *cfg) { return cfg->C <= 8 ? 8 : 32; }
 
 // Validate a config; on success *heads receives B*H.
 dl_status check_config(const dl_config *cfg, size_t *heads) {
@@ -117,7 +128,7 @@ dl_status check_args(const dl_config *cfg, const dl_step_args *a) {
 
 dl_status launch(const dl_config *cfg, int mode, const dlk::StepParams &p, void *stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int cmax = cfg->C <= 8 ? 8 : 32;
+    const int cmax = cmax_of(cfg);
     const int bf16 = cfg->in_dtype == DL_BF16;
     hipError_t e;
     switch (cfg->op) {
@@ -154,6 +165,7 @@ void set_log(dlk::StepParams &p, const dl_state *h) {
     p.logK = h->logK;
     p.logG = h->logG;
     p.L = h->L;
+    p.prep = h->prep;
     if (h->slots) {
         p.slot_base = h->slot_base;
         p.slot_active = h->slot_active;
@@ -200,6 +212,7 @@ dl_status init_handle(dl_state **out, const dl_config *cfg, float *base, void *w
     h->slot_base = reinterpret_cast<int *>(ws + l.sb);
     h->slot_active = reinterpret_cast<unsigned char *>(ws + l.sa);
     h->step = 0;
+    h->prep = nullptr;
     if (slots) {
         h->h_base.assign(cfg->B, 0u);
         h->h_active.assign(cfg->B, 0);
@@ -311,7 +324,13 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
         return DL_OK;
     }
     const bool fold = h->L + 1 == h->cfg.C;
-    st = launch(&h->cfg, fold ? dlk::MODE_MERGE : dlk::MODE_APPEND, p, stream);
+    if (fold || !h->prep) {
+        st = launch(&h->cfg, fold ? dlk::MODE_MERGE : dlk::MODE_APPEND, p, stream);
+    } else {
+        // split replay: the key-side stage once per head, then the tiles
+        st = launch(&h->cfg, dlk::MODE_PREP, p, stream);
+        if (st == DL_OK) st = launch(&h->cfg, dlk::MODE_PREPPED, p, stream);
+    }
     if (st != DL_OK) return st;
     h->L = fold ? 0 : h->L + 1;
     return DL_OK;
@@ -328,7 +347,7 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     for (int t = 0; t < K; ++t)
         if ((st = check_args(&h->cfg, &args[t])) != DL_OK) return st;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int cmax = h->cfg.C <= 8 ? 8 : 32;
+    const int cmax = cmax_of(&h->cfg);
     const int bf16 = h->cfg.in_dtype == DL_BF16;
     for (int t0 = 0; t0 < K;) {
         const int k1 = std::min(K - t0, h->cfg.C - h->L);  // the part that fits the log
@@ -411,6 +430,85 @@ dl_status dl_materialize(const dl_state *h, float *dst, void *stream) {
 }
 
 int dl_log_length(const dl_state *h) { return (h && !h->slots) ? h->L : -1; }
+
+size_t dl_prep_bytes(const dl_config *cfg) {
+    size_t heads = 0;
+    if (check_config(cfg, &heads) != DL_OK) return 0;
+    return heads * (size_t)dlk::prep_stride(cfg->dk, cmax_of(cfg)) * 4;
+}
+
+dl_status dl_set_split_replay(dl_state *h, void *prep, size_t prep_bytes) {
+    if (!h) return fail(DL_ERR_ARG, "handle is NULL");
+    if (h->slots) return fail(DL_ERR_UNSUPPORTED, "split replay needs a lockstep handle");
+    if (!prep) {
+        h->prep = nullptr;
+        return DL_OK;
+    }
+    if (!aligned16(prep)) return fail(DL_ERR_ARG, "prep must be 16-byte aligned");
+    const size_t need = dl_prep_bytes(&h->cfg);
+    if (prep_bytes < need)
+        return fail(DL_ERR_WORKSPACE, "prep is smaller than dl_prep_bytes(cfg) = " + std::to_string(need));
+    h->prep = static_cast<float *>(prep);
+    return DL_OK;
+}
+
+dl_status dl_graph_capture_cycle(dl_graph **out, dl_state *h, const dl_step_args *args) {
+    if (!out) return fail(DL_ERR_ARG, "out is NULL");
+    *out = nullptr;
+    if (!h) return fail(DL_ERR_ARG, "handle is NULL");
+    if (h->slots) return fail(DL_ERR_UNSUPPORTED, "graph capture needs a lockstep handle");
+    if (h->L != 0) return fail(DL_ERR_ARG, "a cycle is captured at an empty log (dl_log_length() == 0)");
+    if (!args) return fail(DL_ERR_ARG, "args is NULL");
+    dl_status st;
+    for (int t = 0; t < h->cfg.C; ++t)
+        if ((st = check_args(&h->cfg, &args[t])) != DL_OK) return st;
+    hipStream_t cs = nullptr;
+    hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+    if (e != hipSuccess) return fail(DL_ERR_HIP, std::string("hipStreamCreate: ") + hipGetErrorString(e));
+    e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+    if (e != hipSuccess) {
+        (void)hipStreamDestroy(cs);
+        return fail(DL_ERR_HIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(e));
+    }
+    // recording runs nothing; a whole cycle brings L back to 0 either way
+    st = DL_OK;
+    for (int t = 0; t < h->cfg.C && st == DL_OK; ++t) st = dl_decode_step(h, &args[t], cs);
+    hipGraph_t g = nullptr;
+    const hipError_t ee = hipStreamEndCapture(cs, &g);
+    h->L = 0;
+    (void)hipStreamDestroy(cs);
+    if (st != DL_OK || ee != hipSuccess) {
+        if (g) (void)hipGraphDestroy(g);
+        return st != DL_OK ? st : fail(DL_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(ee));
+    }
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) return fail(DL_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+    dl_graph *gr = new (std::nothrow) dl_graph;
+    if (!gr) {
+        (void)hipGraphExecDestroy(exec);
+        return fail(DL_ERR_ARG, "out of host memory");
+    }
+    gr->h = h;
+    gr->exec = exec;
+    *out = gr;
+    return DL_OK;
+}
+
+dl_status dl_graph_launch(dl_graph *g, void *stream) {
+    if (!g) return fail(DL_ERR_ARG, "graph is NULL");
+    if (g->h->L != 0) return fail(DL_ERR_ARG, "the handle's log is not empty: a cycle replays at L == 0");
+    const hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(DL_ERR_HIP, std::string("hipGraphLaunch: ") + hipGetErrorString(e));
+    return DL_OK;
+}
+
+void dl_graph_destroy(dl_graph *g) {
+    if (!g) return;
+    (void)hipGraphExecDestroy(g->exec);
+    delete g;
+}
 
 dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *a, void *stream) {
     size_t heads = 0;

@@ -13,7 +13,19 @@ enum { OP_GDN = 0, OP_KDA = 1, OP_RWKV6 = 2 };
 //   EAGER   decode a token directly on a dense state (no log), rewrite it
 //   FOLD    write base + log (L entries) to dst; no token
 //   AUTO    per slot: APPEND, or MERGE when the token fills the slot's log
-enum { MODE_APPEND = 0, MODE_MERGE = 1, MODE_EAGER = 2, MODE_FOLD = 3, MODE_AUTO = 4 };
+//   PREP    split replay, first stage: once per head (one workgroup each),
+//           the token's key-side preparation -- scaled key and query, the
+//           replay coefficients of the L logged entries and <k,q> -- written
+//           to a prep record, and the key side of entry L appended
+//   PREPPED split replay, second stage: APPEND with the key side read from
+//           the prep record instead of computed
+enum { MODE_APPEND = 0, MODE_MERGE = 1, MODE_EAGER = 2, MODE_FOLD = 3, MODE_AUTO = 4, MODE_PREP = 5,
+       MODE_PREPPED = 6 };
+
+// Floats in one head's prep record for head width D and log bound cmax:
+// [0, D) scaled key, [D, 2D) scaled query (or receptance), then cmax key-side
+// and cmax query-side replay coefficients, then the token's scalar term.
+constexpr int prep_stride(int D, int cmax) { return 2 * D + 2 * cmax + 4; }
 
 struct StepParams {
     float *base;         // [N][D][D] fp32 base (or dense state for EAGER)
@@ -38,6 +50,7 @@ struct StepParams {
     const int *slot_base;              // [B] decode-step index of the slot's last empty log
     const unsigned char *slot_active;  // [B] 1 = decode this slot
     unsigned step;                     // decode steps issued so far
+    float *prep;                       // [N][prep_stride(D, cmax)] split-replay records
 };
 
 // Launch one mode for one operator.  in_bf16 selects the input dtype, D the

@@ -11,6 +11,7 @@
 //           base from registers (base read once, written once)
 //   EAGER   the dense recurrence directly (base read once, written once)
 //   FOLD    base + log written to a destination (merge / materialise)
+//   PREP / PREPPED  the two stages of the split-replay variant (below)
 //
 // The method (DeltaLog; gist.science summary, sections "Meccanismo Core" and
 // "Implementazione del Kernel"): the state is split along the value width;
@@ -20,7 +21,10 @@
 // slot-head; here every workgroup recomputes it in its prologue, from LDS,
 // while its base loads are in flight -- a few hundred FLOPs per head against
 // a 32 KB stream, cheaper than a second launch -- and the two tiles of a head
-// run on the same XCD so the second reads the key-side log from L2.
+// run on the same XCD so the second reads the key-side log from L2.  The
+// pages' staged form is built too, for comparison: PREP runs that prologue
+// once per head and stores its results in a small per-head record, and
+// PREPPED is the append whose workgroups read the record instead.
 //
 // Algebra, per head, with cumulative base-2 log-decays g (reset at a fold):
 //   logical state   S_L = diag(2^{g_L}) Sbar + sum_{i<L} diag(2^{g_L-g_i}) k_i x_i^T
@@ -171,7 +175,10 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     constexpr bool LOGGED = MODE != MODE_EAGER;  // reads a log
     constexpr bool TOKEN = MODE != MODE_FOLD;    // decodes a token
     constexpr bool AUTO = MODE == MODE_AUTO;     // append or fold, per slot, at run time
-    constexpr bool CAN_WRITE = MODE != MODE_APPEND;  // may write a dense state
+    constexpr bool PREP = MODE == MODE_PREP;     // split replay: key-side stage, no tile
+    constexpr bool PREPPED = MODE == MODE_PREPPED;  // split replay: key side from the record
+    constexpr bool CAN_WRITE =                   // may write a dense state
+        MODE == MODE_MERGE || MODE == MODE_EAGER || MODE == MODE_FOLD || MODE == MODE_AUTO;
     constexpr int CP = LOGGED ? CMAX : 4;        // entry slots in LDS (multiple of 4)
     constexpr int KPASS = LOGGED ? (CMAX + EPP - 1) / EPP : 1;
     constexpr int XR = LOGGED ? (CMAX + RPP - 1) / RPP : 1;  // log value rows per thread
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     int n, tile;
-    block_to_tile(blockIdx.x, p.N, NTILE, n, tile);
+    block_to_tile(blockIdx.x, p.N, PREP ? 1 : NTILE, n, tile);
     const int C = p.C;
     int L = LOGGED ? p.L : 0;
     if (LOGGED && p.slot_base != nullptr) {
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     // What this workgroup does (uniform across it): compile-time except in
     // AUTO mode, where the token that fills the log also folds it.
     const bool fold = AUTO ? (L + 1 == C) : MODE == MODE_MERGE;
-    const bool append = AUTO ? !fold : MODE == MODE_APPEND;
+    const bool append = AUTO ? !fold : (MODE == MODE_APPEND || PREP || PREPPED);
     const bool writes = AUTO ? fold : CAN_WRITE;  // writes a dense state
     const bool cur_in_log = fold && DELTA;        // fold the token as entry L
     const int last = L > 0 ? L - 1 : 0;  // newest log entry (clamp target of masked loads)
@@ -229,15 +236,18 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     float alpha = 1.f, beta = 0.f;
     TIn vraw = {};
     if (TOKEN) {
-        kraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.k) + (size_t)n * D + c4);
-        qraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.q) + (size_t)n * D + c4);
-        if (GDN)
-            alpha = p.decay[n];
-        else
-            dec4 = *reinterpret_cast<const f4 *>(p.decay + (size_t)n * D + c4);
-        if (DELTA) beta = p.beta[n];
-        if (OP == OP_RWKV6) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
-        vraw = static_cast<const TIn *>(p.v)[(size_t)n * D + col0 + tid % TV];  // used by tid < TV
+        if (!PREPPED) {
+            kraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.k) + (size_t)n * D + c4);
+            qraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.q) + (size_t)n * D + c4);
+            if (GDN)
+                alpha = p.decay[n];
+            else
+                dec4 = *reinterpret_cast<const f4 *>(p.decay + (size_t)n * D + c4);
+        }
+        if (DELTA && !PREP) beta = p.beta[n];
+        if (OP == OP_RWKV6 && !PREPPED)
+            bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
+        if (!PREP) vraw = static_cast<const TIn *>(p.v)[(size_t)n * D + col0 + tid % TV];  // used by tid < TV
     }
     // A2. The log: cumulative log-decay of the newest entry, the key side of
     //     this thread's entries and, in the thread's own row slots (entries
@@ -248,7 +258,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     float glog_s[KPASS];
     f4 glog4[KPASS];
     RawX xrow[XR];
-    if (LOGGED) {
+    if (LOGGED && !PREPPED) {
         const size_t el = (size_t)n * C + last;
         if (GDN)
             glast_s = p.logG[el];
@@ -263,10 +273,22 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             else
                 glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * D + c4);
         }
+    }
+    if (LOGGED && !PREP) {
         const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0 + 4 * cg;
 #pragma unroll
         for (int j = 0; j < XR; ++j)
             xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * D);
+    }
+    // A2'. Split replay: this head's prep record (thread t takes float t of
+    //      the scaled key | scaled query and one coefficient).
+    float pre_mv = 0.f, pre_coef = 0.f, pre_dot = 0.f;
+    if (PREPPED) {
+        static_assert(!PREPPED || 2 * D == NT, "one record float of the scaled vectors per thread");
+        const float *rec = p.prep + (size_t)n * prep_stride(D, CMAX);
+        pre_mv = rec[tid];
+        pre_coef = rec[2 * D + tid % (2 * CP)];
+        pre_dot = rec[2 * D + 2 * CP];
     }
 
     // A3. The base tile: nearly all of the traffic, issued last so that the
@@ -276,10 +298,20 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
     const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
     f4 s[R];
+    if (!PREP) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
+        for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
+    }
 
     // ---------------- Phase B: key-side preparation into LDS ----------------
+    if constexpr (PREPPED) {
+        if (tid < D)
+            s_mv0[tid] = pre_mv;
+        else
+            s_mv1[tid - D] = pre_mv;
+        if (tid < 2 * CP) (&s_coef[0][0])[tid] = pre_coef;
+        if (tid == 0) s_dot = pre_dot;
+    } else {
     const f4 k = TOKEN ? In4<TIn>::unpack(kraw) : f4{0.f, 0.f, 0.f, 0.f};
     const f4 q = TOKEN ? In4<TIn>::unpack(qraw) : f4{0.f, 0.f, 0.f, 0.f};
     const f4 dv = GDN ? f4{alpha, alpha, alpha, alpha} : dec4;
@@ -388,7 +420,21 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             }
         }
     }
+    }  // phase B computed here (not PREPPED)
     __syncthreads();
+
+    if constexpr (PREP) {
+        // split replay, first stage: store the record and leave
+        float *rec = p.prep + (size_t)n * prep_stride(D, CMAX);
+        static_assert(!PREP || 2 * D == NT, "one record float of the scaled vectors per thread");
+        if (DELTA || tid >= D) rec[tid] = tid < D ? s_mv0[tid] : s_mv1[tid - D];
+        if (tid < L) {
+            rec[2 * D + tid] = s_coef[0][tid];
+            rec[2 * D + CP + tid] = s_coef[1][tid];
+        }
+        if (tid == 0) rec[2 * D + 2 * CP] = s_dot;
+        return;
+    }
 
     if (TOKEN) {
         // ---------------- Phase C: matrix-vector products ----------------
@@ -508,7 +554,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
 template <int OP, typename TIn, int D, int MODE, int CMAX>
 hipError_t launch_one(const StepParams &p, hipStream_t s) {
     constexpr int TV = Shape<D>::TV, NT = Shape<D>::NT;
-    const unsigned blocks = (unsigned)p.N * (D / TV);
+    const unsigned blocks = (unsigned)p.N * (MODE == MODE_PREP ? 1 : D / TV);
     hipLaunchKernelGGL((step_kernel<OP, TIn, D, TV, NT, MODE, CMAX>), dim3(blocks), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
@@ -529,6 +575,12 @@ hipError_t launch_mode(int mode, int cmax, const StepParams &p, hipStream_t s) {
         case MODE_AUTO:
             return small ? launch_one<OP, TIn, D, MODE_AUTO, 8>(p, s)
                          : launch_one<OP, TIn, D, MODE_AUTO, 32>(p, s);
+        case MODE_PREP:
+            return small ? launch_one<OP, TIn, D, MODE_PREP, 8>(p, s)
+                         : launch_one<OP, TIn, D, MODE_PREP, 32>(p, s);
+        case MODE_PREPPED:
+            return small ? launch_one<OP, TIn, D, MODE_PREPPED, 8>(p, s)
+                         : launch_one<OP, TIn, D, MODE_PREPPED, 32>(p, s);
         case MODE_EAGER:
             return launch_one<OP, TIn, D, MODE_EAGER, 4>(p, s);
         default:

@@ -63,9 +63,11 @@ class DeltaLogState:
     place at every fold.  The workspace is allocated here with torch.  With
     ``slots=True`` every slot keeps its own log length (continuous batching):
     slots start inactive and are switched with ``activate`` / ``deactivate``.
+    ``split_replay=True`` runs each append as the staged pair (a once-per-head
+    key-side launch, then the value tiles) with a prep buffer allocated here.
     """
 
-    def __init__(self, op, in_dtype, base, C, slots=False):
+    def __init__(self, op, in_dtype, base, C, slots=False, split_replay=False):
         if op not in B.OP_CODES or in_dtype not in B.DTYPE_CODES:
             raise ValueError(f"unknown op {op!r} or dtype {in_dtype!r}")
         if base.dim() != 4:
@@ -86,6 +88,18 @@ class DeltaLogState:
                                                 _stream(self.device))
         else:
             self.handle = B.dl_state_init(self.cfg, base.data_ptr(), self.workspace.data_ptr(), nbytes)
+        self.prep = None
+        if split_replay:
+            self.set_split_replay(True)
+
+    def set_split_replay(self, on):
+        """Switch between the fused (False) and the split (True) replay preparation."""
+        if on:
+            if self.prep is None:
+                self.prep = torch.empty(B.dl_prep_bytes(self.cfg), dtype=torch.uint8, device=self.device)
+            B.dl_set_split_replay(self.handle, self.prep.data_ptr(), self.prep.numel())
+        else:
+            B.dl_set_split_replay(self.handle, 0, 0)
 
     def step(self, q, k, v, beta, decay, bonus=None, out=None):
         """Decode one token for all heads; returns out [B, H, dv] fp32."""
@@ -115,6 +129,16 @@ class DeltaLogState:
 
     def step_packed(self, args, stream=None):
         B.dl_decode_step(self.handle, args, _stream(self.device) if stream is None else stream)
+
+    def capture_cycle(self, tokens):
+        """Record one merge cycle as a HIP graph.  ``tokens`` holds C dicts of the
+        step inputs (q, k, v, beta, decay, bonus, out); the graph replays on those
+        same tensors, so refill them in place between replays."""
+        if len(tokens) != self.C:
+            raise ValueError(f"a cycle is {self.C} tokens, got {len(tokens)}")
+        args = [self.step_args(t["q"], t["k"], t["v"], t.get("beta"), t["decay"], t.get("bonus"), t["out"])
+                for t in tokens]
+        return CycleGraph(self, B.dl_graph_capture_cycle(self.handle, args), tokens)
 
     def merge(self):
         B.dl_merge(self.handle, _stream(self.device))
@@ -157,6 +181,28 @@ class DeltaLogState:
         if getattr(self, "handle", None):
             B.dl_state_destroy(self.handle)
             self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class CycleGraph:
+    """One captured merge cycle of a DeltaLogState (dl_graph_capture_cycle)."""
+
+    def __init__(self, state, graph, tokens):
+        self.state, self.graph = state, graph
+        self._keep = tokens  # the recorded tensors must outlive the graph
+
+    def launch(self, stream=None):
+        B.dl_graph_launch(self.graph, _stream(self.state.device) if stream is None else stream)
+
+    def close(self):
+        if getattr(self, "graph", None):
+            B.dl_graph_destroy(self.graph)
+            self.graph = None
 
     def __del__(self):
         try:

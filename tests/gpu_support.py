@@ -59,8 +59,9 @@ def _token(dev, t):
 
 
 def run_deltalog(dev, op, in_dtype, C, T=None, state_steps=(), heads=None, merge_after=(),
-                 materialize_every_step=False, on_step=None):
-    """Decode T tokens through dl_decode_step.
+                 materialize_every_step=False, on_step=None, split_replay=False):
+    """Decode T tokens through dl_decode_step (appends in the split-replay
+    form with ``split_replay``).
 
     Returns (outputs [T,B,H,dv] on the device, {t: materialised state of the
     selected heads after t tokens, on the CPU}, the DeltaLogState).
@@ -69,7 +70,7 @@ def run_deltalog(dev, op, in_dtype, C, T=None, state_steps=(), heads=None, merge
     Tfull, Bsz, H, d = q.shape
     T = Tfull if T is None else T
     base = dev["S0"].clone()
-    st = dl.DeltaLogState(op, in_dtype, base, C)
+    st = dl.DeltaLogState(op, in_dtype, base, C, split_replay=split_replay)
     outs = torch.empty((T, Bsz, H, d), dtype=torch.float32, device=q.device)
     hsel = None if heads is None else torch.as_tensor(np.asarray(heads), dtype=torch.long, device=q.device)
     want = set(state_steps)

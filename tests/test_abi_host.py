@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 23, names
     for name in names:
         assert hasattr(lib, name), f"{name} is declared in deltalog.h but not exported"
     for name in names:
@@ -187,6 +187,40 @@ def test_slot_calls_validate_on_the_host():
     with pytest.raises(dl.DeltaLogError):
         dl.dl_state_init_slots(B.Config(0, 1, 0, 4, 64, 64, 4), FAKE, FAKE, 1 << 20)
     assert lib.dl_slot_log_length(None, 0) == -1
+
+
+def test_prep_bytes():
+    # N records of 2*dk + 2*M + 4 floats, M = 8 for C <= 8 and 32 above
+    assert dl.dl_prep_bytes(dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)) == 8 * (128 + 16 + 4) * 4
+    assert dl.dl_prep_bytes(dl.make_config("kda", "bf16", 2, 4, 64, 64, 13)) == 8 * (128 + 64 + 4) * 4
+    assert dl.dl_prep_bytes(dl.make_config("rwkv6", "f32", 128, 32, 64, 64, 8)) == 4096 * (128 + 16 + 4) * 4
+    assert dl.dl_prep_bytes(B.Config(0, 1, 2, 4, 48, 48, 4)) == 0
+
+
+def test_split_replay_and_graph_validate_on_the_host():
+    cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)
+    lib = B.load_library()
+    need = dl.dl_prep_bytes(cfg)
+    assert lib.dl_set_split_replay(None, FAKE, need) == B.DL_ERR_ARG
+    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    try:
+        assert lib.dl_set_split_replay(h, FAKE + 8, need) == B.DL_ERR_ARG  # misaligned
+        assert lib.dl_set_split_replay(h, FAKE, need - 4) == B.DL_ERR_WORKSPACE
+        assert lib.dl_set_split_replay(h, FAKE, need) == B.DL_OK
+        assert lib.dl_set_split_replay(h, None, 0) == B.DL_OK  # back to the fused form
+        g = ctypes.c_void_p()
+        arr = (B.StepArgs * 4)(*([_args()] * 4))
+        assert lib.dl_graph_capture_cycle(None, h, arr) == B.DL_ERR_ARG
+        assert lib.dl_graph_capture_cycle(ctypes.byref(g), None, arr) == B.DL_ERR_ARG
+        assert lib.dl_graph_capture_cycle(ctypes.byref(g), h, None) == B.DL_ERR_ARG
+        bad = (B.StepArgs * 4)(_args(), _args(), _args(), _args(q=0))  # the last token is bad
+        assert lib.dl_graph_capture_cycle(ctypes.byref(g), h, bad) == B.DL_ERR_ARG
+        assert g.value is None
+        assert dl.dl_log_length(h) == 0
+    finally:
+        dl.dl_state_destroy(h)
+    assert lib.dl_graph_launch(None, None) == B.DL_ERR_ARG
+    lib.dl_graph_destroy(None)
 
 
 def test_eager_step_rejects_bad_state():

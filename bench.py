@@ -476,10 +476,16 @@ def staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K):
 
 
 def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs):
-    """Per-launch event times with a 512 MB write between launches (flushes the MALL)."""
+    """Per-launch event times with a 512 MB read between launches, outside the
+    events: the read refills the 256 MB Infinity Cache with clean lines of
+    another buffer, so each launch finds none of its data cached (a write
+    would leave dirty lines whose write-back the next launch would pay)."""
     import numpy as np
     import torch
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    torch.sum(flush, dim=0, out=sink)
+    torch.cuda.synchronize()
     base = d["S0"].clone()
     st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
     ncyc = 6
@@ -487,7 +493,7 @@ def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs):
     tok = 0
     for c in range(ncyc):
         for i in range(C):
-            flush.fill_(float(c * C + i))
+            torch.sum(flush, dim=0, out=sink)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             t = tok % w.T

@@ -1,0 +1,31 @@
+"""bench.py's command-line contract, on the CPU (no kernel runs here)."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench(*args, env=None):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                          stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=120, env=env)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = _bench("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_world_size_above_one_is_refused():
+    env = dict(os.environ, WORLD_SIZE="4")
+    r = _bench(env=env)
+    assert r.returncode == 2
+
+
+def test_help_lists_the_options():
+    r = _bench("--help")
+    assert r.returncode == 0
+    for opt in ("--steps", "--warmup", "--workload", "--C", "--cold", "--tokens", "--split-ablation",
+                "--staggered", "--calibrate-copy"):
+        assert opt in r.stdout

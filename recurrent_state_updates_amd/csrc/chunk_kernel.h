@@ -40,14 +40,17 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     using Raw = typename In4<TIn>::raw;
     using RawX = typename In4<TX>::raw;
     static_assert(KM <= EPP, "one key-side group per token");
+    static_assert(R % 4 == 0, "a thread's rows of the scaled vectors are read as float4");
     static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
 
     __shared__ __attribute__((aligned(16))) float s_k[KM][D];      // token keys
     __shared__ __attribute__((aligned(16))) float s_q[KM][D];      // token queries (receptances)
     __shared__ __attribute__((aligned(16))) float s_lg[KM][GW];    // log2 of each token's decay
     __shared__ __attribute__((aligned(16))) float s_g[KM + 1][GW]; // g_{t-1} at index t (g_{-1} = g_L)
-    __shared__ __attribute__((aligned(16))) float s_mv0[KM][D];    // 2^{rho_t} k_t
-    __shared__ __attribute__((aligned(16))) float s_mv1[KM][D];    // 2^{rho_t} q_t (r_t)
+    // 2^{rho_t} k_t and 2^{rho_t} q_t (r_t), row r stored at (r % RPP) * R + r / RPP so
+    // that the R rows of one thread (rs, rs + RPP, ...) are contiguous
+    __shared__ __attribute__((aligned(16))) float s_mv0[KM][D];
+    __shared__ __attribute__((aligned(16))) float s_mv1[KM][D];
     __shared__ __attribute__((aligned(16))) float s_scale[D];      // fold: 2^{g_{K-1}} per row
     __shared__ __attribute__((aligned(16))) float s_kt[CP * D];    // fold: decayed keys [entry][row]
     __shared__ __attribute__((aligned(16))) float s_x[CP * TV];    // fold: value factors [entry][col]
@@ -170,12 +173,9 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     };
 
     // ---------------- Phase B2: per token: scaled key / query, dot, log append ----------------
-    if (ke < K) {
-        const int t = ke;
-        const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
-        const f4 sc = exp2v(rho);
-        *reinterpret_cast<f4 *>(&s_mv0[t][c4]) = sc * kt_in;
-        *reinterpret_cast<f4 *>(&s_mv1[t][c4]) = sc * qt_in;
+    {
+        // every group reduces its (valid, clamped) token's dot so that the lane
+        // exchanges run with the whole wave active
         float part;
         if (DELTA) {
             part = dot4(kt_in, qt_in);
@@ -183,8 +183,21 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             const f4 bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
             part = dot4(qt_in * bon4, kt_in);
         }
-        part = group_sum<KL>(part);
-        if (c4 == 0) s_dot[t] = part;
+        part = group_sum_valu<KL>(part);
+        if (ke < K && c4 == 0) s_dot[ke] = part;
+    }
+    if (ke < K) {
+        const int t = ke;
+        const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
+        const f4 sc = exp2v(rho);
+        const f4 m0 = sc * kt_in, m1 = sc * qt_in;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int row = c4 + c;
+            const int at = (row % RPP) * R + row / RPP;
+            s_mv0[t][at] = m0[c];
+            s_mv1[t][at] = m1[c];
+        }
         if (!fold && tile == 0) {  // entry L + t of the log: the key copy and its log-decay
             const size_t e = (size_t)n * C + L + t;
             *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * D + c4) = kraw;
@@ -215,17 +228,31 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             ke4 = f4{0.f, 0.f, 0.f, 0.f};
             ge4 = f4{0.f, 0.f, 0.f, 0.f};
         }
-        for (int t = 0; t < K; ++t) {
-            const bool valid = is_old || (is_new && e - L < t);
-            const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
-            f4 kt = valid ? ke4 * exp2v(rho - ge4) : f4{0.f, 0.f, 0.f, 0.f};
-            float pk = dot4(kt, *reinterpret_cast<const f4 *>(&s_k[t][c4]));
-            float pq = dot4(kt, *reinterpret_cast<const f4 *>(&s_q[t][c4]));
-            pk = group_sum<KL>(pk);
-            pq = group_sum<KL>(pq);
-            if (c4 == 0 && e < NE) {
-                s_coef[0][t][e] = valid ? pk : 0.f;
-                s_coef[1][t][e] = valid ? pq : 0.f;
+        // every token's partial dots first, then one batch of lane reductions
+        float pk[KM], pq[KM];
+#pragma unroll
+        for (int t = 0; t < KM; ++t) {
+            pk[t] = 0.f;
+            pq[t] = 0.f;
+            if (t < K && (is_old || (is_new && e - L < t))) {
+                const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
+                const f4 kt = ke4 * exp2v(rho - ge4);
+                pk[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_k[t][c4]));
+                pq[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_q[t][c4]));
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < KM; ++t) {
+            pk[t] = group_sum_valu<KL>(pk[t]);
+            pq[t] = group_sum_valu<KL>(pq[t]);
+        }
+        if (c4 == 0 && e < NE) {
+#pragma unroll
+            for (int t = 0; t < KM; ++t) {
+                if (t < K) {
+                    s_coef[0][t][e] = pk[t];
+                    s_coef[1][t][e] = pq[t];
+                }
             }
         }
         if (fold && (is_old || is_new))
@@ -249,13 +276,19 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     __syncthreads();
 
     // ---------------- Phase C: base products of every token from the register tile ----------------
-    for (int t = 0; t < K; ++t) {
+#pragma unroll
+    for (int t = 0; t < KM; ++t) {
+        if (t >= K) break;
         f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int row = rs + RPP * i;
-            if (DELTA) y += s[i] * s_mv0[t][row];
-            z += s[i] * s_mv1[t][row];
+        for (int i4 = 0; i4 < R / 4; ++i4) {
+            const f4 a = *reinterpret_cast<const f4 *>(&s_mv0[t][rs * R + 4 * i4]);
+            const f4 b = *reinterpret_cast<const f4 *>(&s_mv1[t][rs * R + 4 * i4]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (DELTA) y += s[4 * i4 + c] * a[c];
+                z += s[4 * i4 + c] * b[c];
+            }
         }
 #pragma unroll
         for (int j = 0; j < XR; ++j) {
@@ -267,17 +300,9 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             }
         }
 #pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) {
-            if (DELTA) {
-                y.x += __shfl_xor(y.x, off);
-                y.y += __shfl_xor(y.y, off);
-                y.z += __shfl_xor(y.z, off);
-                y.w += __shfl_xor(y.w, off);
-            }
-            z.x += __shfl_xor(z.x, off);
-            z.y += __shfl_xor(z.y, off);
-            z.z += __shfl_xor(z.z, off);
-            z.w += __shfl_xor(z.w, off);
+        for (int c = 0; c < 4; ++c) {
+            if (DELTA) y[c] = column_sum_valu<LPR>(y[c]);
+            z[c] = column_sum_valu<LPR>(z[c]);
         }
         if (lane < LPR) {
             if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][wave][0][4 * cg]) = y;

@@ -146,6 +146,55 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Lane exchanges that stay in the VALU (no LDS round trip): DPP moves within
+// rows of 16 lanes and the gfx950 permlane swaps across rows.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_XOR8 = 0x128;        // row_ror:8 (within a row of 16, a rotation by 8 is xor 8)
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i -> 7 - i within each group of 8
+constexpr int DPP_MIRROR = 0x140;      // lane i -> 15 - i within each row
+
+// x[l] + x[l ^ 16]: the swap returns the lane's even-row and odd-row values.
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x[l] + x[l ^ 32]: the swap returns the lane's low-half and high-half values.
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over aligned groups of W lanes.  Each step adds two values already equal
+// across their sub-groups, so the mirrors act as exchanges between sub-groups
+// and every lane of a group ends with the same bits.
+template <int W>
+__device__ __forceinline__ float group_sum_valu(float x) {
+    static_assert(W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32 || W == 64, "group width");
+    if (W >= 2) x += dpp_mov<DPP_XOR1>(x);
+    if (W >= 4) x += dpp_mov<DPP_XOR2>(x);
+    if (W >= 8) x += dpp_mov<DPP_HALF_MIRROR>(x);
+    if (W >= 16) x += dpp_mov<DPP_MIRROR>(x);
+    if (W >= 32) x = xor16_sum(x);
+    if (W >= 64) x = xor32_sum(x);
+    return x;
+}
+
+// Sum over the lanes of a wave that share l % P (P = 8, 16 or 32 lanes per row
+// of a tile): the partial products of one value column.
+template <int P>
+__device__ __forceinline__ float column_sum_valu(float x) {
+    static_assert(P == 8 || P == 16 || P == 32 || P == 64, "lanes per tile row");
+    if (P <= 8) x += dpp_mov<DPP_XOR8>(x);
+    if (P <= 16) x = xor16_sum(x);
+    if (P <= 32) x = xor32_sum(x);
+    return x;
+}
+
 // Optional occupancy floor in waves per SIMD (0: the compiler's choice).  A
 // floor that forces spills has been seen to place register copies inside a
 // lane-masked branch (the value of only the active lanes is kept), so the

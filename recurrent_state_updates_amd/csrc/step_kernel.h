@@ -138,14 +138,6 @@ __device__ __forceinline__ void block_to_tile(int b, int N, int ntile, int &n, i
     tile = g - n * ntile;
 }
 
-// Sum over aligned groups of W consecutive lanes.
-template <int W>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int off = W / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
-
 // Lane exchanges that stay in the VALU (no LDS round trip): DPP moves within
 // rows of 16 lanes and the gfx950 permlane swaps across rows.
 template <int CTRL>
@@ -408,7 +400,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     if (TOKEN) {
         // every key-side group holds all D channels, so each group's sum is complete
         float part = DELTA ? dot4(k, q) : dot4(q * bon4, k);
-        part = group_sum<KL>(part);
+        part = group_sum_valu<KL>(part);
         if (tid == 0) s_dot = part;
     }
     if (LOGGED) {
@@ -431,12 +423,9 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         }
         if (TOKEN) {
 #pragma unroll
-            for (int off = KL / 2; off >= 1; off >>= 1) {
-#pragma unroll
-                for (int ps = 0; ps < KPASS; ++ps) {
-                    pk[ps] += __shfl_xor(pk[ps], off);
-                    pq[ps] += __shfl_xor(pq[ps], off);
-                }
+            for (int ps = 0; ps < KPASS; ++ps) {
+                pk[ps] = group_sum_valu<KL>(pk[ps]);
+                pq[ps] = group_sum_valu<KL>(pq[ps]);
             }
             if (c4 == 0) {
 #pragma unroll
@@ -508,17 +497,9 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             }
         }
 #pragma unroll
-        for (int off = LPR; off < 64; off <<= 1) {
-            if (DELTA) {
-                y.x += __shfl_xor(y.x, off);
-                y.y += __shfl_xor(y.y, off);
-                y.z += __shfl_xor(y.z, off);
-                y.w += __shfl_xor(y.w, off);
-            }
-            z.x += __shfl_xor(z.x, off);
-            z.y += __shfl_xor(z.y, off);
-            z.z += __shfl_xor(z.z, off);
-            z.w += __shfl_xor(z.w, off);
+        for (int c = 0; c < 4; ++c) {
+            if (DELTA) y[c] = column_sum_valu<LPR>(y[c]);
+            z[c] = column_sum_valu<LPR>(z[c]);
         }
         if (lane < LPR) {
             if (DELTA) *reinterpret_cast<f4 *>(&s_red[wave][0][4 * cg]) = y;

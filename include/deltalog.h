@@ -232,6 +232,19 @@ dl_status dl_slot_deactivate(dl_state *h, int slot, void *stream);
  * slot or a lockstep handle. */
 int dl_slot_log_length(const dl_state *h, int slot);
 
+/* Write the logical state of one slot, [H,dk,dv] fp32, into dst (for
+ * example to save a request that leaves); nothing else changes.  Lockstep
+ * and per-slot handles; one launch over the slot's H heads only.  dst must
+ * not overlap the slot's base block.  DL_ERR_ARG for a bad slot, an inactive
+ * slot of a per-slot handle, or a bad dst. */
+dl_status dl_materialize_slot(const dl_state *h, int slot, float *dst, void *stream);
+
+/* Fold one active slot's log into its base block now (an early merge of that
+ * slot alone, output-neutral); the slot's log becomes empty.  Per-slot
+ * handles only (DL_ERR_ARG otherwise, or for a bad or inactive slot); a
+ * no-op when the slot's log is empty. */
+dl_status dl_slot_merge(dl_state *h, int slot, void *stream);
+
 /* The eager dense update for comparison (gist.science "Problema"): reads
  * the [B,H,dk,dv] fp32 state, writes out = o_t and the updated state in
  * place.  Uses only cfg's op, in_dtype, B, H, dk, dv (C is ignored). */

@@ -78,6 +78,8 @@ def load_library():
         "dl_slot_activate": (i, [vp, i, vp]),
         "dl_slot_deactivate": (i, [vp, i, vp]),
         "dl_slot_log_length": (i, [vp, i]),
+        "dl_materialize_slot": (i, [vp, i, vp, vp]),
+        "dl_slot_merge": (i, [vp, i, vp]),
         "dl_predict_token_us": (ctypes.c_double, [cp, ctypes.c_double, ctypes.c_double]),
         "dl_choose_capacity": (i, [cp, i, ctypes.c_double, ctypes.c_double]),
         "dl_prep_bytes": (sz, [cp]),
@@ -144,6 +146,14 @@ def dl_slot_deactivate(handle, slot, stream=0):
 
 def dl_slot_log_length(handle, slot):
     return int(load_library().dl_slot_log_length(handle, slot))
+
+
+def dl_materialize_slot(handle, slot, dst, stream=0):
+    _check(load_library().dl_materialize_slot(handle, slot, dst, stream))
+
+
+def dl_slot_merge(handle, slot, stream=0):
+    _check(load_library().dl_slot_merge(handle, slot, stream))
 
 
 def dl_decode_step(handle, args, stream=0):

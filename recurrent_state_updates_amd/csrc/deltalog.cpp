@@ -429,7 +429,57 @@ dl_status dl_materialize(const dl_state *h, float *dst, void *stream) {
     return launch(&h->cfg, dlk::MODE_FOLD, p, stream);
 }
 
+// A FOLD launch over the H heads of one slot: every pointer moves to that
+// slot's heads, so the kernel sees a batch of one (its slot index is 0).
+dlk::StepParams slot_fold_params(const dl_state *h, int slot, float *dst) {
+    const dl_config &c = h->cfg;
+    const size_t head0 = (size_t)slot * (size_t)c.H;
+    const size_t xs = c.op == DL_RWKV6 ? in_size(c.in_dtype) : 4;
+    const size_t gw = c.op == DL_GDN ? 1 : (size_t)c.dk;
+    dlk::StepParams p = params_of(&c, (size_t)c.H);
+    p.base = h->base + head0 * (size_t)c.dk * (size_t)c.dv;
+    p.dst = dst;
+    p.logX = static_cast<char *>(h->logX) + head0 * (size_t)c.C * (size_t)c.dv * xs;
+    p.logK = static_cast<char *>(h->logK) + head0 * (size_t)c.C * (size_t)c.dk * in_size(c.in_dtype);
+    p.logG = h->logG + head0 * (size_t)c.C * gw;
+    p.L = h->L;
+    p.prep = nullptr;
+    if (h->slots) {
+        p.slot_base = h->slot_base + slot;
+        p.slot_active = h->slot_active + slot;
+        p.step = h->step;
+    }
+    return p;
+}
+
 int dl_log_length(const dl_state *h) { return (h && !h->slots) ? h->L : -1; }
+
+dl_status dl_materialize_slot(const dl_state *h, int slot, float *dst, void *stream) {
+    if (!h) return fail(DL_ERR_ARG, "handle is NULL");
+    if (slot < 0 || slot >= h->cfg.B) return fail(DL_ERR_ARG, "slot out of range");
+    if (!dst) return fail(DL_ERR_ARG, "dst is NULL");
+    if (!aligned16(dst)) return fail(DL_ERR_ARG, "dst must be 16-byte aligned");
+    const size_t blk = (size_t)h->cfg.H * (size_t)h->cfg.dk * (size_t)h->cfg.dv;
+    const float *b0 = h->base + (size_t)slot * blk;
+    if (dst < b0 + blk && b0 < dst + blk) return fail(DL_ERR_ARG, "dst must not overlap the slot's base");
+    if (h->slots && !h->h_active[slot]) return fail(DL_ERR_ARG, "slot is not active");
+    return launch(&h->cfg, dlk::MODE_FOLD, slot_fold_params(h, slot, dst), stream);
+}
+
+dl_status dl_slot_merge(dl_state *h, int slot, void *stream) {
+    if (!h || !h->slots) return fail(DL_ERR_ARG, "handle is NULL or not a per-slot handle");
+    if (slot < 0 || slot >= h->cfg.B) return fail(DL_ERR_ARG, "slot out of range");
+    if (!h->h_active[slot]) return fail(DL_ERR_ARG, "slot is not active");
+    if (slot_length(h, slot) == 0) return DL_OK;
+    const size_t head0 = (size_t)slot * (size_t)h->cfg.H;
+    dl_status st = launch(&h->cfg, dlk::MODE_FOLD,
+                          slot_fold_params(h, slot, h->base + head0 * (size_t)h->cfg.dk * (size_t)h->cfg.dv), stream);
+    if (st != DL_OK) return st;
+    // the slot's log is now empty: its origin moves to this step
+    if ((st = slot_set(h, slot, 1, (int)h->step, 0, 0, 0, stream)) != DL_OK) return st;
+    h->h_base[slot] = h->step;
+    return DL_OK;
+}
 
 size_t dl_prep_bytes(const dl_config *cfg) {
     size_t heads = 0;

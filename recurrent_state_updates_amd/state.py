@@ -163,6 +163,18 @@ class DeltaLogState:
     def slot_log_length(self, slot):
         return B.dl_slot_log_length(self.handle, slot)
 
+    def materialize_slot(self, slot, dst=None):
+        """The logical [H, dk, dv] state of one slot (e.g. of a request that leaves)."""
+        if dst is None:
+            dst = torch.empty(tuple(self.base.shape[1:]), dtype=torch.float32, device=self.device)
+        _check_tensor("dst", dst, tuple(self.base.shape[1:]), torch.float32, self.device)
+        B.dl_materialize_slot(self.handle, slot, dst.data_ptr(), _stream(self.device))
+        return dst
+
+    def merge_slot(self, slot):
+        """Fold one slot's log into its base block now (per-slot handles)."""
+        B.dl_slot_merge(self.handle, slot, _stream(self.device))
+
     def workspace_views(self):
         """(X, K, G) views of the log for inspection: [B,H,C,dv], [B,H,C,dk], [B,H,C(,dk)]."""
         ox, ok, og = B.dl_workspace_layout(self.cfg)

@@ -36,7 +36,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 25, names
     for name in names:
         assert hasattr(lib, name), f"{name} is declared in deltalog.h but not exported"
     for name in names:
@@ -187,6 +187,25 @@ def test_slot_calls_validate_on_the_host():
     with pytest.raises(dl.DeltaLogError):
         dl.dl_state_init_slots(B.Config(0, 1, 0, 4, 64, 64, 4), FAKE, FAKE, 1 << 20)
     assert lib.dl_slot_log_length(None, 0) == -1
+
+
+def test_per_slot_fold_calls_validate_on_the_host():
+    cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)
+    lib = B.load_library()
+    dst = FAKE + 0x20000000
+    assert lib.dl_materialize_slot(None, 0, dst, None) == B.DL_ERR_ARG
+    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    try:
+        for slot in (-1, 2):
+            assert lib.dl_materialize_slot(h, slot, dst, None) == B.DL_ERR_ARG
+        assert lib.dl_materialize_slot(h, 0, None, None) == B.DL_ERR_ARG
+        assert lib.dl_materialize_slot(h, 0, dst + 8, None) == B.DL_ERR_ARG  # misaligned
+        blk = 4 * 64 * 64 * 4  # one slot's [H, dk, dv] fp32
+        assert lib.dl_materialize_slot(h, 1, FAKE + blk + 256, None) == B.DL_ERR_ARG  # inside slot 1's base
+        assert lib.dl_slot_merge(h, 0, None) == B.DL_ERR_ARG  # a lockstep handle has no per-slot logs
+    finally:
+        dl.dl_state_destroy(h)
+    assert lib.dl_slot_merge(None, 0, None) == B.DL_ERR_ARG
 
 
 def test_prep_bytes():

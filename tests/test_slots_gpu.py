@@ -110,3 +110,97 @@ def test_continuous_batching_schedule(op, C):
         assert np.isnan(o[~active, b]).all()
     # slot 3 ended before T: materialise leaves inactive slots untouched
     assert np.isnan(fin[3]).all()
+
+
+@pytest.mark.parametrize("op,slots", [("gdn", False), ("kda", True), ("rwkv6", True), ("rwkv6", False)])
+def test_materialize_slot_is_the_slice_of_the_full_state(op, slots):
+    T, Bsz, H, d, C = 6, 3, 2, 64, 4
+    x = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=51)
+    dev = gs.to_device(x, DEV)
+    base = dev["S0"].clone()
+    st = dl.DeltaLogState(op, "bf16", base, C, slots=slots)
+    if slots:
+        for b in range(Bsz):
+            st.activate(b)
+    for t in range(T):  # ends mid-cycle: the log is not empty
+        st.step(**_token(dev, t))
+    full = st.materialize()
+    for b in range(Bsz):
+        one = st.materialize_slot(b)
+        torch.cuda.synchronize()
+        assert torch.equal(one, full[b]), b
+
+
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_slot_merge_is_output_neutral_and_local(op):
+    """Folding one slot's log early changes no output and empties only that log."""
+    T, Bsz, H, d, C = 14, 3, 2, 64, 4
+    x = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=52)
+    dev = gs.to_device(x, DEV)
+    runs = []
+    for merge in (False, True):
+        base = dev["S0"].clone()
+        st = dl.DeltaLogState(op, "bf16", base, C, slots=True)
+        for b in range(Bsz):
+            st.activate(b)
+        outs = torch.empty((T, Bsz, H, d), dtype=torch.float32, device=DEV)
+        for t in range(T):
+            st.step(out=outs[t], **_token(dev, t))
+            if merge and t in (2, 9):
+                lengths = [st.slot_log_length(b) for b in range(Bsz)]
+                st.merge_slot(1)
+                assert st.slot_log_length(1) == 0
+                assert [st.slot_log_length(b) for b in (0, 2)] == [lengths[0], lengths[2]]
+        torch.cuda.synchronize()
+        runs.append(outs.cpu())
+    assert max(gs.rel(runs[1][t], runs[0][t]) for t in range(T)) <= 1e-5
+    ref = gs.oracle_run(x, op)
+    o = runs[1].numpy().reshape(T, Bsz * H, d)
+    assert max(gs.rel(o[t], ref["out"][t]) for t in range(T)) <= gs.OUT_GATE
+
+
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_evict_and_resume_a_request(op):
+    """Slot 1's request is saved with materialize_slot and leaves at token 5;
+    another request uses the slot for a while; the first one comes back at
+    token 9 from its saved state and continues with its own tokens 5..T-1:
+    its outputs equal the oracle of its uninterrupted sequence."""
+    T, Bsz, H, d, C = 13, 2, 2, 64, 4
+    x = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=53)
+    other = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=54)
+    dev, dev_o = gs.to_device(x, DEV), gs.to_device(other, DEV)
+    base = dev["S0"].clone()
+    st = dl.DeltaLogState(op, "bf16", base, C, slots=True)
+    st.activate(0)
+    st.activate(1)
+    outs = torch.full((T, Bsz, H, d), float("nan"), dtype=torch.float32, device=DEV)
+    for t in range(5):
+        st.step(out=outs[t], **_token(dev, t))
+    saved = st.materialize_slot(1)
+    st.deactivate(1)
+    base[1].copy_(dev_o["S0"][1])  # another request takes the slot
+    st.activate(1)
+    for t in range(5, 9):  # slot 0 keeps its own tokens; slot 1 decodes the other request's
+        tok = _token(dev, t)
+        tok_o = _token(dev_o, t)
+        mixed = {k: (None if v is None else (v if k == "bonus" else torch.stack([v[0], tok_o[k][1]])))
+                 for k, v in tok.items()}
+        st.step(out=outs[t], **mixed)
+    st.deactivate(1)
+    base[1].copy_(saved)  # the first request returns
+    st.activate(1)
+    # slot 1 continues with its own tokens 5.. while slot 0 continues with tokens 9..
+    resumed = torch.empty((T - 9, Bsz, H, d), dtype=torch.float32, device=DEV)
+    for i in range(T - 9):
+        t0, t1 = 9 + i, 5 + i
+        tok0, tok1 = _token(dev, t0), _token(dev, t1)
+        mixed = {k: (None if v is None else (v if k == "bonus" else torch.stack([v[0], tok1[k][1]])))
+                 for k, v in tok0.items()}
+        st.step(out=resumed[i], **mixed)
+    torch.cuda.synchronize()
+    ref = gs.oracle_run(x, op)  # both slots' uninterrupted sequences
+    ro = ref["out"].reshape(T, Bsz, H, d)
+    r = resumed.cpu().numpy()
+    n = T - 9
+    assert max(gs.rel(r[i, 1], ro[5 + i, 1]) for i in range(n)) <= gs.OUT_GATE  # slot 1 resumed
+    assert max(gs.rel(r[i, 0], ro[9 + i, 0]) for i in range(n)) <= gs.OUT_GATE  # slot 0 uninterrupted

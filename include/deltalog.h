@@ -168,7 +168,7 @@ int dl_log_length(const dl_state *h);
  * equal the fused path up to fp32 rounding.
  *
  * dl_prep_bytes: bytes of that buffer for cfg (N records of 2*dk + 2*M + 4
- * fp32, M = 8 for C <= 8 and 32 otherwise); 0 for an invalid cfg.
+ * fp32, M the smallest of 8, 16 and 32 not below C); 0 for an invalid cfg.
  * dl_set_split_replay: prep = device memory of at least dl_prep_bytes bytes,
  * 16-byte aligned, owned by the caller and outliving its use (it holds no
  * state between steps), or NULL to return to the fused form.  Lockstep

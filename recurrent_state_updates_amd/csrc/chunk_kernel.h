@@ -386,14 +386,19 @@ hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int OP, typename TIn, int D>
+hipError_t launch_chunk_bounded(int cmax, const ChunkParams &p, hipStream_t s) {
+    if (cmax <= 8) return launch_chunk_one<OP, TIn, D, 8>(p, s);
+    if (cmax <= 16) return launch_chunk_one<OP, TIn, D, 16>(p, s);
+    return launch_chunk_one<OP, TIn, D, 32>(p, s);
+}
+
 template <int OP, typename TIn>
 hipError_t launch_chunk_width(int D, int cmax, const ChunkParams &p, hipStream_t s) {
-    const bool small = cmax <= 8;
     switch (D) {
-        case 32: return small ? launch_chunk_one<OP, TIn, 32, 8>(p, s) : launch_chunk_one<OP, TIn, 32, 32>(p, s);
-        case 64: return small ? launch_chunk_one<OP, TIn, 64, 8>(p, s) : launch_chunk_one<OP, TIn, 64, 32>(p, s);
-        case 128:
-            return small ? launch_chunk_one<OP, TIn, 128, 8>(p, s) : launch_chunk_one<OP, TIn, 128, 32>(p, s);
+        case 32: return launch_chunk_bounded<OP, TIn, 32>(cmax, p, s);
+        case 64: return launch_chunk_bounded<OP, TIn, 64>(cmax, p, s);
+        case 128: return launch_chunk_bounded<OP, TIn, 128>(cmax, p, s);
         default: return hipErrorInvalidValue;
     }
 }

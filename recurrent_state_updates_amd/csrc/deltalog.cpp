@@ -62,7 +62,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 size_t in_size(int dtype) { return dtype == DL_BF16 ? 2 : 4; }
 
 // Compile-time bound on log entries of the kernels that serve capacity C.
-int cmax_of(const dl_config *cfg) { return cfg->C <= 8 ? 8 : 32; }
+int cmax_of(const dl_config *cfg) { return cfg->C <= 8 ? 8 : (cfg->C <= 16 ? 16 : 32); }
 
 // Validate a config; on success *heads receives B*H.
 dl_status check_config(const dl_config *cfg, size_t *heads) {

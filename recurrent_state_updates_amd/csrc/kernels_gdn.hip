@@ -1,5 +1,5 @@
 // Kernel instantiations for the GDN operator (see step_kernel.h).
-#include "step_kernel.h"
+#include "step_launch.h"
 
 namespace dlk {
 

@@ -1,5 +1,5 @@
 // Kernel instantiations for the RWKV6 operator (see step_kernel.h).
-#include "step_kernel.h"
+#include "step_launch.h"
 
 namespace dlk {
 

@@ -54,7 +54,7 @@ struct StepParams {
 };
 
 // Launch one mode for one operator.  in_bf16 selects the input dtype, D the
-// head width (dk == dv), cmax the compile-time bound on log entries (8 or 32).
+// head width (dk == dv), cmax the compile-time bound on log entries (8, 16 or 32).
 hipError_t launch_gdn(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
 hipError_t launch_kda(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
 hipError_t launch_rwkv6(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);

@@ -581,57 +581,4 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     }
 }
 
-template <int OP, typename TIn, int D, int MODE, int CMAX>
-hipError_t launch_one(const StepParams &p, hipStream_t s) {
-    constexpr int TV = Shape<D>::TV, NT = Shape<D>::NT;
-    const unsigned blocks = (unsigned)p.N * (MODE == MODE_PREP ? 1 : D / TV);
-    hipLaunchKernelGGL((step_kernel<OP, TIn, D, TV, NT, MODE, CMAX>), dim3(blocks), dim3(NT), 0, s, p);
-    return hipGetLastError();
-}
-
-template <int OP, typename TIn, int D>
-hipError_t launch_mode(int mode, int cmax, const StepParams &p, hipStream_t s) {
-    const bool small = cmax <= 8;
-    switch (mode) {
-        case MODE_APPEND:
-            return small ? launch_one<OP, TIn, D, MODE_APPEND, 8>(p, s)
-                         : launch_one<OP, TIn, D, MODE_APPEND, 32>(p, s);
-        case MODE_MERGE:
-            return small ? launch_one<OP, TIn, D, MODE_MERGE, 8>(p, s)
-                         : launch_one<OP, TIn, D, MODE_MERGE, 32>(p, s);
-        case MODE_FOLD:
-            return small ? launch_one<OP, TIn, D, MODE_FOLD, 8>(p, s)
-                         : launch_one<OP, TIn, D, MODE_FOLD, 32>(p, s);
-        case MODE_AUTO:
-            return small ? launch_one<OP, TIn, D, MODE_AUTO, 8>(p, s)
-                         : launch_one<OP, TIn, D, MODE_AUTO, 32>(p, s);
-        case MODE_PREP:
-            return small ? launch_one<OP, TIn, D, MODE_PREP, 8>(p, s)
-                         : launch_one<OP, TIn, D, MODE_PREP, 32>(p, s);
-        case MODE_PREPPED:
-            return small ? launch_one<OP, TIn, D, MODE_PREPPED, 8>(p, s)
-                         : launch_one<OP, TIn, D, MODE_PREPPED, 32>(p, s);
-        case MODE_EAGER:
-            return launch_one<OP, TIn, D, MODE_EAGER, 4>(p, s);
-        default:
-            return hipErrorInvalidValue;
-    }
-}
-
-template <int OP, typename TIn>
-hipError_t launch_width(int D, int mode, int cmax, const StepParams &p, hipStream_t s) {
-    switch (D) {
-        case 32: return launch_mode<OP, TIn, 32>(mode, cmax, p, s);
-        case 64: return launch_mode<OP, TIn, 64>(mode, cmax, p, s);
-        case 128: return launch_mode<OP, TIn, 128>(mode, cmax, p, s);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <int OP>
-hipError_t launch_op(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s) {
-    return in_bf16 ? launch_width<OP, bf16_bits>(D, mode, cmax, p, s)
-                   : launch_width<OP, float>(D, mode, cmax, p, s);
-}
-
 }  // namespace dlk

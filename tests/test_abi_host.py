@@ -209,9 +209,10 @@ def test_per_slot_fold_calls_validate_on_the_host():
 
 
 def test_prep_bytes():
-    # N records of 2*dk + 2*M + 4 floats, M = 8 for C <= 8 and 32 above
+    # N records of 2*dk + 2*M + 4 floats, M the smallest of 8, 16, 32 not below C
     assert dl.dl_prep_bytes(dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)) == 8 * (128 + 16 + 4) * 4
-    assert dl.dl_prep_bytes(dl.make_config("kda", "bf16", 2, 4, 64, 64, 13)) == 8 * (128 + 64 + 4) * 4
+    assert dl.dl_prep_bytes(dl.make_config("kda", "bf16", 2, 4, 64, 64, 13)) == 8 * (128 + 32 + 4) * 4
+    assert dl.dl_prep_bytes(dl.make_config("kda", "bf16", 2, 4, 64, 64, 17)) == 8 * (128 + 64 + 4) * 4
     assert dl.dl_prep_bytes(dl.make_config("rwkv6", "f32", 128, 32, 64, 64, 8)) == 4096 * (128 + 16 + 4) * 4
     assert dl.dl_prep_bytes(B.Config(0, 1, 2, 4, 48, 48, 4)) == 0
 

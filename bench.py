@@ -34,10 +34,16 @@ KERNEL_SOURCES = ["recurrent_state_updates_amd/csrc/step_kernel.h",
 
 
 def kernel_source_hash():
+    """First 16 hex digits of the SHA-256 of the kernel sources with comments
+    and blank space removed: the counters are tied to the code, not to its
+    commentary."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("\n".join(ln.strip() for ln in text.splitlines() if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,12 +1,16 @@
 // deltalog.cpp -- the C ABI declared in include/deltalog.h: argument
 // validation, the host-side log-length bookkeeping and kernel dispatch.
 //
-// The handle lives in host memory only.  The log length L is the same for
-// every slot and head (lockstep batch decode), so it is tracked here and
-// passed to each launch; the launch mode follows from (L, C): append while
-// L + 1 < C, and decode + fold when the token fills the log (the
-// signal-papers summary, caption of Fig. 4: append while L < C, materialise
-// when L = C).
+// The handle lives in host memory only.  On a lockstep handle the log length
+// L is the same for every slot and head, so it is tracked here and passed to
+// each launch; the launch mode follows from (L, C): append while L + 1 < C,
+// and decode + fold when the token fills the log (the signal-papers summary,
+// caption of Fig. 4: append while L < C, materialise when L = C).  On a
+// per-slot handle each slot's length is (steps issued - the slot's origin)
+// mod C; the origins live in the workspace, written in stream order by a
+// small kernel, and the workgroups of one launch read them to choose between
+// appending and folding.  A host mirror of the origins serves validation and
+// dl_slot_log_length.
 #include "../../include/deltalog.h"
 
 #include <hip/hip_runtime.h>

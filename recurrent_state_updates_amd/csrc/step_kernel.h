@@ -11,6 +11,8 @@
 //           base from registers (base read once, written once)
 //   EAGER   the dense recurrence directly (base read once, written once)
 //   FOLD    base + log written to a destination (merge / materialise)
+//   AUTO    per-slot logs: a slot's workgroups APPEND, or MERGE when this
+//           token fills that slot's log
 //   PREP / PREPPED  the two stages of the split-replay variant (below)
 //
 // The method (DeltaLog; gist.science summary, sections "Meccanismo Core" and
@@ -18,13 +20,15 @@
 // each work unit owns a base slice and its value-side log shard, and the
 // key-side factors and log-decay metadata are shared by the tiles.  The
 // pages run the key-side replay preparation as a separate stage once per
-// slot-head; here every workgroup recomputes it in its prologue, from LDS,
-// while its base loads are in flight -- a few hundred FLOPs per head against
-// a 32 KB stream, cheaper than a second launch -- and the two tiles of a head
-// run on the same XCD so the second reads the key-side log from L2.  The
-// pages' staged form is built too, for comparison: PREP runs that prologue
-// once per head and stores its results in a small per-head record, and
-// PREPPED is the append whose workgroups read the record instead.
+// slot-head; here every workgroup recomputes it in its prologue, from
+// registers, while its base loads are in flight -- a few hundred FLOPs per
+// head against a 32 KB stream -- and the two tiles of a head run on the same
+// XCD so the second reads the key-side log from L2.  The pages' staged form
+// is built too, for comparison: PREP runs that prologue once per head and
+// stores its results in a small per-head record, and PREPPED is the append
+// whose workgroups read the record instead.  On MI355X the staged form costs
+// about 5 us more per append: its first stage is a serial, latency-bound
+// launch.
 //
 // Algebra, per head, with cumulative base-2 log-decays g (reset at a fold):
 //   logical state   S_L = diag(2^{g_L}) Sbar + sum_{i<L} diag(2^{g_L-g_i}) k_i x_i^T

@@ -22,9 +22,12 @@ SOURCES = ["deltalog.cpp", "kernels_gdn.hip", "kernels_kda.hip", "kernels_rwkv6.
            "kernels_gdn_chunk.hip", "kernels_kda_chunk.hip", "kernels_rwkv6_chunk.hip"]
 
 # Packed fp32 VALU ops are switched off for all device code; the host pass
-# prints that it does not know the feature, which is harmless.
+# prints that it does not know the feature, which is harmless.  Matrix-core
+# accumulators are kept in ordinary VGPRs: gfx950 has one register file for
+# both kinds, and accumulators in AGPRs would cost a wave of occupancy.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-I", os.path.join(ROOT, "include")]
 
 

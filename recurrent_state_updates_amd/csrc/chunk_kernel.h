@@ -24,7 +24,9 @@
 
 namespace dlk {
 
-template <int OP, typename TIn, int D, int TV, int NT, int CMAX>
+// MM selects the matrix-core form of the token products (phase C); it needs
+// 16 lanes per tile row and pays off from about three tokens on.
+template <int OP, typename TIn, int D, int TV, int NT, int CMAX, bool MM>
 __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     using G = Geom<D, TV, NT>;
     constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
@@ -276,37 +278,88 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     __syncthreads();
 
     // ---------------- Phase C: base products of every token from the register tile ----------------
-#pragma unroll
-    for (int t = 0; t < KM; ++t) {
-        if (t >= K) break;
-        f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+    static_assert(!MM || (LPR == 16 && 2 * KM == 16), "matrix-core form: 16 lanes per row, 16 vectors");
+    if constexpr (MM) {
+        // On the matrix cores: P[m][col] = sum_row A[m][row] S[row][col] over this
+        // wave's rows, with the 16 vectors m = (side, token) = (m / 8, m % 8):
+        // side 0 the scaled keys, side 1 the scaled queries (receptances).  The
+        // register tile already has the 16x16x4 operand layout: in k-step i,
+        // lane l holds row 4 wave + l/16 + RPP i and columns 4 (l % 16) + c, so
+        // component c of s[i] is the B operand of the c-th product, and lane l
+        // supplies A[l % 16][that row].  The old log joins as XR more k-steps
+        // with the replay coefficients as A and the logged value rows as B.
+        typedef float m4 __attribute__((ext_vector_type(4)));
+        const int m = lane & 15;
+        const int kr = lane >> 4;
+        const int side = m >> 3, tm = m & 7;
+        const bool live = tm < K;
+        const float *mv = side ? &s_mv1[tm][0] : &s_mv0[tm][0];
+        float a[R];
 #pragma unroll
         for (int i4 = 0; i4 < R / 4; ++i4) {
-            const f4 a = *reinterpret_cast<const f4 *>(&s_mv0[t][rs * R + 4 * i4]);
-            const f4 b = *reinterpret_cast<const f4 *>(&s_mv1[t][rs * R + 4 * i4]);
+            const f4 v = *reinterpret_cast<const f4 *>(&mv[(4 * wave + kr) * R + 4 * i4]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (DELTA) y += s[4 * i4 + c] * a[c];
-                z += s[4 * i4 + c] * b[c];
-            }
+            for (int c = 0; c < 4; ++c) a[4 * i4 + c] = live ? v[c] : 0.f;
+        }
+        m4 acc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = m4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], s[i][c], acc[c], 0, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < XR; ++j) {
-            const int i = rs + RPP * j;
-            if (i < L) {
-                const f4 x = In4<TX>::unpack(xrow[j]);
-                if (DELTA) y += s_coef[0][t][i] * x;
-                z += s_coef[1][t][i] * x;
-            }
-        }
+            // entries at or past L were loaded from a clamped index and may be
+            // anything (an unused slot holds whatever the workspace held): zero
+            // both operands, since 0 * NaN would poison the sum
+            const int e = rs + RPP * j;  // rs = 4 wave + kr
+            const float co = (live && e < L) ? s_coef[side][tm][e] : 0.f;
+            const f4 xv = e < L ? In4<TX>::unpack(xrow[j]) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (DELTA) y[c] = column_sum_valu<LPR>(y[c]);
-            z[c] = column_sum_valu<LPR>(z[c]);
+            for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(co, xv[c], acc[c], 0, 0, 0);
         }
-        if (lane < LPR) {
-            if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][wave][0][4 * cg]) = y;
-            *reinterpret_cast<f4 *>(&s_red[t][wave][1][4 * cg]) = z;
+        // lane l holds P[4 (l / 16) + q][4 (l % 16) + c] in acc[c][q]
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int mo = 4 * kr + q;
+            *reinterpret_cast<f4 *>(&s_red[mo & 7][wave][mo >> 3][4 * m]) =
+                f4{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < KM; ++t) {
+            if (t >= K) break;
+            f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int i4 = 0; i4 < R / 4; ++i4) {
+                const f4 a = *reinterpret_cast<const f4 *>(&s_mv0[t][rs * R + 4 * i4]);
+                const f4 b = *reinterpret_cast<const f4 *>(&s_mv1[t][rs * R + 4 * i4]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (DELTA) y += s[4 * i4 + c] * a[c];
+                    z += s[4 * i4 + c] * b[c];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < XR; ++j) {
+                const int i = rs + RPP * j;
+                if (i < L) {
+                    const f4 x = In4<TX>::unpack(xrow[j]);
+                    if (DELTA) y += s_coef[0][t][i] * x;
+                    z += s_coef[1][t][i] * x;
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (DELTA) y[c] = column_sum_valu<LPR>(y[c]);
+                z[c] = column_sum_valu<LPR>(z[c]);
+            }
+            if (lane < LPR) {
+                if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][wave][0][4 * cg]) = y;
+                *reinterpret_cast<f4 *>(&s_red[t][wave][1][4 * cg]) = z;
+            }
         }
     }
     __syncthreads();
@@ -382,7 +435,16 @@ template <int OP, typename TIn, int D, int CMAX>
 hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
     constexpr int TV = Shape<D>::TV, NT = Shape<D>::NT;
     const unsigned blocks = (unsigned)p.N * (D / TV);
-    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX>), dim3(blocks), dim3(NT), 0, s, p);
+    // matrix cores for the token products at d = 128 from three tokens on
+    // (measured: fewer tokens, or the 16 KB tiles of d = 64, run faster on
+    // the vector ALUs)
+    if constexpr (D == 128) {
+        if (p.K >= 3) {
+            hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, true>), dim3(blocks), dim3(NT), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, false>), dim3(blocks), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 

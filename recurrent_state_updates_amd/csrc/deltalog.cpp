@@ -345,11 +345,16 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     size_t heads = 0;
     dl_status st = check_config(&h->cfg, &heads);
     if (st != DL_OK) return st;
-    if (h->slots) return fail(DL_ERR_UNSUPPORTED, "multi-token decode needs a lockstep handle");
     if (!args) return fail(DL_ERR_ARG, "args is NULL");
     if (K < 1 || K > DL_MAX_TOKENS) return fail(DL_ERR_SHAPE, "K must lie in [1, 8]");
     for (int t = 0; t < K; ++t)
         if ((st = check_args(&h->cfg, &args[t])) != DL_OK) return st;
+    if (h->slots) {
+        // every slot's log fills at its own token: one per-slot step per token
+        for (int t = 0; t < K; ++t)
+            if ((st = dl_decode_step(h, &args[t], stream)) != DL_OK) return st;
+        return DL_OK;
+    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int cmax = cmax_of(&h->cfg);
     const int bf16 = h->cfg.in_dtype == DL_BF16;

@@ -204,3 +204,35 @@ def test_evict_and_resume_a_request(op):
     n = T - 9
     assert max(gs.rel(r[i, 1], ro[5 + i, 1]) for i in range(n)) <= gs.OUT_GATE  # slot 1 resumed
     assert max(gs.rel(r[i, 0], ro[9 + i, 0]) for i in range(n)) <= gs.OUT_GATE  # slot 0 uninterrupted
+
+
+@pytest.mark.parametrize("op", ["gdn", "rwkv6"])
+def test_tokens_on_a_per_slot_handle_equal_single_steps(op):
+    """dl_decode_tokens on a per-slot handle (slots started at different
+    tokens, so their logs fill at different tokens) equals one step per token."""
+    T, Bsz, H, d, C = 12, 3, 2, 64, 4
+    x = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=55)
+    dev = gs.to_device(x, DEV)
+    chunks = [(0, 1), (1, 2), (2, 5), (5, 12)]  # slot b joins at token b
+    runs = []
+    for fused in (False, True):
+        base = dev["S0"].clone()
+        st = dl.DeltaLogState(op, "bf16", base, C, slots=True)
+        outs = torch.full((T, Bsz, H, d), float("nan"), dtype=torch.float32, device=DEV)
+        for t0, t1 in chunks:
+            if t0 < Bsz:
+                st.activate(t0)
+            if fused:
+                tok = {k: (v if v is None or k == "bonus" else v[t0:t1]) for k, v in dev.items()
+                       if k in ("q", "k", "v", "beta", "decay", "bonus")}
+                st.step_tokens(out=outs[t0:t1], **tok)
+            else:
+                for t in range(t0, t1):
+                    st.step(out=outs[t], **_token(dev, t))
+        torch.cuda.synchronize()
+        runs.append((outs.cpu(), st.materialize().cpu(), [st.slot_log_length(b) for b in range(Bsz)]))
+    # slots not yet started keep their NaN outputs in both runs
+    assert torch.equal(torch.isnan(runs[0][0]), torch.isnan(runs[1][0]))
+    assert torch.equal(torch.nan_to_num(runs[0][0]), torch.nan_to_num(runs[1][0]))
+    assert torch.equal(runs[0][1], runs[1][1])
+    assert runs[0][2] == runs[1][2]

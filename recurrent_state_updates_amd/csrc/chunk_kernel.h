@@ -413,16 +413,44 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         f4 acc[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rs + RPP * i];
-        for (int e = 0; e < NE; e += 4) {
-            const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + 4 * cg]);
-            const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + 4 * cg]);
-            const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + 4 * cg]);
-            const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + 4 * cg]);
+        if constexpr (MM) {
+            // The rank-NE update on the matrix cores.  For row group g and
+            // column offset c: P[M][n] = sum_e kt[e][row(M)] x[e][4 n + c] with
+            // row(M) = 4 wave + M / 4 + RPP (4 g + M % 4), so that lane l ends
+            // with P[4 (l / 16) + q][l % 16] = the update of its own s[4 g + q][c].
+            // The entry slots past NE are zero up to a multiple of four.
+            typedef float m4 __attribute__((ext_vector_type(4)));
+            const int m = lane & 15, kr = lane >> 4;
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                const int row = rs + RPP * i;
-                acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
-                          s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
+            for (int g = 0; g < R / 4; ++g) {
+                const int arow = 4 * wave + (m >> 2) + RPP * (4 * g + (m & 3));
+                m4 pc[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) pc[c] = m4{0.f, 0.f, 0.f, 0.f};
+                for (int e = 0; e < NE; e += 4) {
+                    const float av = s_kt[(e + kr) * D + arow];
+                    const f4 bv = *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + 4 * m]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) pc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[c], pc[c], 0, 0, 0);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[4 * g + q][c] += pc[c][q];
+                }
+            }
+        } else {
+            for (int e = 0; e < NE; e += 4) {
+                const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + 4 * cg]);
+                const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + 4 * cg]);
+                const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + 4 * cg]);
+                const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + 4 * cg]);
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const int row = rs + RPP * i;
+                    acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
+                              s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
+                }
             }
         }
         f4 *dst4 = reinterpret_cast<f4 *>(p.base) + tile4;

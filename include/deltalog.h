@@ -30,9 +30,14 @@
  *  - State buffers (base, dst, state) and the workspace must be 16-byte
  *    aligned; every other device pointer must be aligned to its element
  *    size.  Buffers named as outputs must not overlap inputs unless stated.
- *  - Return values are dl_status codes: DL_OK (0) or a negative error.  On an
- *    error nothing was enqueued and the handle is unchanged;
+ *  - Return values are dl_status codes: DL_OK (0) or a negative error.  Every
+ *    argument is checked before anything is enqueued, so on any error but
+ *    DL_ERR_HIP nothing was enqueued and the handle is unchanged;
  *    dl_last_error() then returns a message naming the argument at fault.
+ *    DL_ERR_HIP means the runtime refused a launch; a call that issues
+ *    several launches may have enqueued the earlier ones, so the handle and
+ *    the device state are then undefined (re-create the handle from a saved
+ *    state).
  *    Faults inside a kernel (e.g. a freed buffer) surface asynchronously at
  *    the caller's next synchronisation, not through these codes.
  *  - A handle is not thread-safe; distinct handles are independent.

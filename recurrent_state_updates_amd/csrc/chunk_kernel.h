@@ -459,9 +459,19 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     }
 }
 
+// Tile shape of the chunk kernel: 64-column value tiles at D = 128 (32 KB,
+// 256 threads; 16 lanes per tile row, the layout of the matrix-core form),
+// whole heads below.  The K tokens' working set in LDS grows with the tile
+// width, so the chunk kernel keeps the narrower tile.
+template <int D>
+struct ChunkShape {
+    static constexpr int TV = D == 128 ? 64 : D;
+    static constexpr int NT = D == 128 ? 256 : (D == 64 ? 128 : 64);
+};
+
 template <int OP, typename TIn, int D, int CMAX>
 hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
-    constexpr int TV = Shape<D>::TV, NT = Shape<D>::NT;
+    constexpr int TV = ChunkShape<D>::TV, NT = ChunkShape<D>::NT;
     const unsigned blocks = (unsigned)p.N * (D / TV);
     // matrix cores for the token products at d = 128 from three tokens on
     // (measured: fewer tokens, or the 16 KB tiles of d = 64, run faster on

@@ -1,7 +1,8 @@
 // step_kernel.h -- the decode-step kernel family for gfx950.
 //
 // One workgroup owns a D x TV tile of one head's fp32 state: all D key rows
-// and TV of the D value columns (the pages' value-tile parallelism).  Its
+// and TV of the D value columns (the pages' value-tile parallelism; the
+// single-token kernels use TV = D, one tile per head, see Shape).  Its
 // threads stream the tile once from HBM with coalesced 16-byte loads (a tile
 // row is TV/4 lanes wide), keep it in registers, and do everything else
 // around that single pass:
@@ -22,8 +23,9 @@
 // pages run the key-side replay preparation as a separate stage once per
 // slot-head; here every workgroup recomputes it in its prologue, from
 // registers, while its base loads are in flight -- a few hundred FLOPs per
-// head against a 32 KB stream -- and the two tiles of a head run on the same
-// XCD so the second reads the key-side log from L2.  The pages' staged form
+// head against a 16-64 KB stream; with one tile per head nothing is
+// recomputed, and with several (the chunk kernel) the tiles of a head run
+// on the same XCD so the later ones read the key-side log from L2.  The pages' staged form
 // is built too, for comparison: PREP runs that prologue once per head and
 // stores its results in a small per-head record, and PREPPED is the append
 // whose workgroups read the record instead.  On MI355X the staged form costs
@@ -120,19 +122,23 @@ struct Geom {
     static_assert(TV <= NT && KL <= 64 && NT % KL == 0, "column stage and key-side groups");
 };
 
-// Tile shape per head width: 32 KB (D = 128, two value tiles per head),
-// 16 KB (D = 64) and 4 KB (D = 32) per workgroup.
+// Tile shape of the single-token kernels: one workgroup per head at every
+// width -- 64 KB and 512 threads at D = 128, 16 KB and 128 threads at D = 64,
+// 4 KB and 64 threads at D = 32 -- eight float4 of the state per thread.  A
+// whole head is one contiguous block, which streams about 7 % faster on
+// MI355X than two 64-column halves of it (rows read as 256-byte pieces at a
+// 512-byte stride), for the append and the fold alike.
 template <int D>
 struct Shape {
-    static constexpr int TV = D == 128 ? 64 : D;
-    static constexpr int NT = D == 128 ? 256 : (D == 64 ? 128 : 64);
+    static constexpr int TV = D;
+    static constexpr int NT = D == 128 ? 512 : (D == 64 ? 128 : 64);
 };
 
 // Workgroups are handed to the eight XCDs round-robin in dispatch order
 // (block b runs on XCD b % 8).  Map block b so that each XCD walks one
-// contiguous range of (head, tile) pairs in order: the two tiles of a head
-// run back to back on the same XCD (the second reads the head's key-side
-// log from that XCD's L2), and each L2 gathers whole contiguous lines of the
+// contiguous range of (head, tile) pairs in order: the tiles of a head run
+// back to back on the same XCD (the later ones read the head's key-side log
+// from that XCD's L2), and each L2 gathers whole contiguous lines of the
 // outputs and log entries it writes instead of every eighth head's pieces.
 __device__ __forceinline__ void block_to_tile(int b, int N, int ntile, int &n, int &tile) {
     const int nb = N * ntile;
@@ -325,13 +331,13 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         for (int j = 0; j < XR; ++j)
             xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * D);
     }
-    // A2'. Split replay: this head's prep record (thread t takes float t of
-    //      the scaled key | scaled query and one coefficient).
+    // A2'. Split replay: this head's prep record (thread t < 2D takes float t
+    //      of the scaled key | scaled query, and one coefficient).
     float pre_mv = 0.f, pre_coef = 0.f, pre_dot = 0.f;
     if (PREPPED) {
-        static_assert(!PREPPED || 2 * D == NT, "one record float of the scaled vectors per thread");
+        static_assert(!PREPPED || 2 * D <= NT, "one record float of the scaled vectors per thread");
         const float *rec = p.prep + (size_t)n * prep_stride(D, CMAX);
-        pre_mv = rec[tid];
+        pre_mv = rec[min(tid, 2 * D - 1)];
         pre_coef = rec[2 * D + tid % (2 * CP)];
         pre_dot = rec[2 * D + 2 * CP];
     }
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     if constexpr (PREPPED) {
         if (tid < D)
             s_mv0[tid] = pre_mv;
-        else
+        else if (tid < 2 * D)
             s_mv1[tid - D] = pre_mv;
         if (tid < 2 * CP) (&s_coef[0][0])[tid] = pre_coef;
         if (tid == 0) s_dot = pre_dot;
@@ -468,8 +474,8 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     if constexpr (PREP) {
         // split replay, first stage: store the record and leave
         float *rec = p.prep + (size_t)n * prep_stride(D, CMAX);
-        static_assert(!PREP || 2 * D == NT, "one record float of the scaled vectors per thread");
-        if (DELTA || tid >= D) rec[tid] = tid < D ? s_mv0[tid] : s_mv1[tid - D];
+        static_assert(!PREP || 2 * D <= NT, "one record float of the scaled vectors per thread");
+        if (tid < 2 * D && (DELTA || tid >= D)) rec[tid] = tid < D ? s_mv0[tid] : s_mv1[tid - D];
         if (tid < L) {
             rec[2 * D + tid] = s_coef[0][tid];
             rec[2 * D + CP + tid] = s_coef[1][tid];

@@ -263,8 +263,10 @@ dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *
  * read_gbps; the token that fills the log moves the base twice, at copy_gbps
  * (gist.science summary, "Modello di Traffico": appends of compact factors,
  * one amortised dense write per interval, replay of the log).  Bandwidths
- * <= 0 select the values these kernels sustain on MI355X (5900 GB/s read,
- * 5750 GB/s read+write).  Host-only.  Returns a negative value for an
+ * <= 0 select the values fitted to these kernels' measured times on MI355X
+ * (6075 GB/s for appends, 5725 GB/s for the fold; within 3 % of the measured
+ * amortised time for C = 1..32 at GDN and KDA B=128 d=128, launch gaps
+ * included).  Host-only.  Returns a negative value for an
  * invalid cfg. */
 double dl_predict_token_us(const dl_config *cfg, double read_gbps, double copy_gbps);
 

@@ -24,6 +24,33 @@
 
 namespace dlk {
 
+// Token pointers of the kernel arguments as opaque scalar values.  The lanes
+// of one wave belong to GPW consecutive key-side groups (tokens t0 .. t0 +
+// GPW - 1, t0 uniform), so each lane chooses among GPW pointers, each a
+// scalar load at a uniform index.  Left visible, the choice would be folded
+// back into an index into the argument array, read with a vector load that
+// the data load must wait for; the empty asm prevents that.  The result is
+// returned as a global-memory pointer (the asm hides where it came from).
+template <typename T>
+__device__ __forceinline__ T opaque_scalar(T x) {
+    asm volatile("" : "+s"(x));
+    return x;
+}
+
+template <typename T>
+using global_ptr = const T __attribute__((address_space(1))) *;
+
+template <typename E, int GPW, typename T>
+__device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS], int t0, int K, int g) {
+    T r = opaque_scalar(arr[min(t0, K - 1)]);
+#pragma unroll
+    for (int i = 1; i < GPW; ++i) {
+        const T c = opaque_scalar(arr[min(t0 + i, K - 1)]);
+        r = g == i ? c : r;
+    }
+    return (global_ptr<E>)static_cast<const E *>(r);
+}
+
 // MM selects the matrix-core form of the token products (phase C); it needs
 // 16 lanes per tile row and pays off from about three tokens on.
 template <int OP, typename TIn, int D, int TV, int NT, int CMAX, bool MM>
@@ -42,6 +69,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     using Raw = typename In4<TIn>::raw;
     using RawX = typename In4<TX>::raw;
     static_assert(KM <= EPP, "one key-side group per token");
+    static_assert(64 % KL == 0, "key-side groups do not straddle waves");
     static_assert(R % 4 == 0, "a thread's rows of the scaled vectors are read as float4");
     static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
 
@@ -59,7 +87,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     __shared__ float s_coef[2][KM][CP];                            // per token, per entry
     __shared__ __attribute__((aligned(16))) float s_red[KM][NW][2][TV];
     __shared__ float s_dot[KM];   // <k_t, q_t> or sum r u k
-    __shared__ float s_beta[KM];
+    __shared__ float s_beta[KM + 1];  // slot KM takes the writes of lanes that hold no token
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -79,20 +107,36 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     const int ke = tid / KL;            // key-side group: token ke, then entries ps*EPP + ke
 
     // ---------------- Phase A: loads (token ke's key side, the old log, the tile) ----------------
-    // token tk = min(ke, K-1): groups beyond the chunk load a valid token and ignore it
-    const int tk = min(ke, K - 1);
-    const Raw kraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.k[tk]) + (size_t)n * D + c4);
-    const Raw qraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.q[tk]) + (size_t)n * D + c4);
+    // group ke takes token min(ke, K-1): groups beyond the chunk load a valid token and ignore it.
+    // Every load of the tokens is issued unconditionally and ahead of the tile,
+    // so that none of them waits for another (loads complete in issue order).
+    constexpr int GPW = 64 / KL;  // key-side groups per wave
+    const int t0 = __builtin_amdgcn_readfirstlane(tid >> 6) * GPW;
+    const int g = lane / KL;      // ke = t0 + g
+    const Raw kraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.k, t0, K, g) + (size_t)n * D + c4);
+    const Raw qraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.q, t0, K, g) + (size_t)n * D + c4);
     f4 dec4 = {1.f, 1.f, 1.f, 1.f};
     float alpha = 1.f;
+    const global_ptr<float> dec_t = group_pick<float, GPW>(p.decay, t0, K, g);
     if (GDN)
-        alpha = p.decay[tk][n];
+        alpha = dec_t[n];
     else
-        dec4 = *reinterpret_cast<const f4 *>(p.decay[tk] + (size_t)n * D + c4);
+        dec4 = *reinterpret_cast<global_ptr<f4>>(dec_t + (size_t)n * D + c4);
+    const float beta_t = DELTA ? group_pick<float, GPW>(p.beta, t0, K, g)[n] : 0.f;
+    f4 bon4 = {0.f, 0.f, 0.f, 0.f};
+    if (!DELTA) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
+    // every token's value at this thread's column; slots past the chunk
+    // re-read token 0 (a valid address) and are never used
     TIn vraw[KM];
+    {
+        const void *v0 = opaque_scalar(p.v[0]);
 #pragma unroll
-    for (int t = 0; t < KM; ++t)
-        vraw[t] = t < K ? static_cast<const TIn *>(p.v[t])[(size_t)n * D + col0 + tid % TV] : TIn{};
+        for (int t = 0; t < KM; ++t) {
+            const void *vt = t == 0 ? v0 : opaque_scalar(p.v[t]);
+            vt = t < K ? vt : v0;
+            vraw[t] = ((global_ptr<TIn>)static_cast<const TIn *>(vt))[(size_t)n * D + col0 + tid % TV];
+        }
+    }
     float glast_s = 0.f;
     f4 glast4 = {0.f, 0.f, 0.f, 0.f};
     Raw klog[KPASS];
@@ -124,6 +168,10 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     f4 s[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
+    // every load above is issued before anything consumes one (a consumer
+    // scheduled among them would wait for all loads issued before it)
+    __builtin_amdgcn_sched_barrier(0);
+    if (DELTA) s_beta[(c4 == 0 && ke < K) ? ke : KM] = beta_t;
 
     // ---------------- Phase B1: every token's inputs into LDS (group ke = token) ----------------
     const f4 kt_in = In4<TIn>::unpack(kraw);
@@ -136,7 +184,6 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         } else {
             *reinterpret_cast<f4 *>(&s_lg[ke][c4]) = log2v(dec4);
         }
-        if (c4 == 0 && DELTA) s_beta[ke] = p.beta[ke][n];
     }
     if (ke == 0) {  // g_{-1} = g_L, newest old entry's cumulative log-decay
         if (GDN) {
@@ -179,12 +226,10 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         // every group reduces its (valid, clamped) token's dot so that the lane
         // exchanges run with the whole wave active
         float part;
-        if (DELTA) {
+        if (DELTA)
             part = dot4(kt_in, qt_in);
-        } else {
-            const f4 bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
+        else
             part = dot4(qt_in * bon4, kt_in);
-        }
         part = group_sum_valu<KL>(part);
         if (ke < K && c4 == 0) s_dot[ke] = part;
     }

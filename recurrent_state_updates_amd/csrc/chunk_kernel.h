@@ -31,6 +31,12 @@ namespace dlk {
 // back into an index into the argument array, read with a vector load that
 // the data load must wait for; the empty asm prevents that.  The result is
 // returned as a global-memory pointer (the asm hides where it came from).
+// The input-dtype bits of a value that was read from that dtype (exact).
+__device__ __forceinline__ void store_raw(float *dst, float x) { *dst = x; }
+__device__ __forceinline__ void store_raw(bf16_bits *dst, float x) {
+    *dst = static_cast<bf16_bits>(__float_as_uint(x) >> 16);
+}
+
 template <typename T>
 __device__ __forceinline__ T opaque_scalar(T x) {
     asm volatile("" : "+s"(x));
@@ -73,19 +79,35 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     static_assert(R % 4 == 0, "a thread's rows of the scaled vectors are read as float4");
     static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
 
-    __shared__ __attribute__((aligned(16))) float s_k[KM][D];      // token keys
-    __shared__ __attribute__((aligned(16))) float s_q[KM][D];      // token queries (receptances)
-    __shared__ __attribute__((aligned(16))) float s_lg[KM][GW];    // log2 of each token's decay
-    __shared__ __attribute__((aligned(16))) float s_g[KM + 1][GW]; // g_{t-1} at index t (g_{-1} = g_L)
+    // LDS.  Phase B's token-side arrays (keys, queries, log-decays, the scaled
+    // vectors) are dead once phase C has read its operands, so in the
+    // matrix-core form the per-wave products of phase C reuse their space (a
+    // barrier separates the last read from the first write); the vector form
+    // reads the scaled vectors while it writes products and keeps both.
+    constexpr int SZ_K = KM * D;               // floats; every size a multiple of 4
+    constexpr int SZ_LG = (KM * GW + 3) & ~3;
+    constexpr int SZ_G = ((KM + 1) * GW + 3) & ~3;
+    constexpr int SZ_B = 4 * SZ_K + SZ_LG + SZ_G;
+    constexpr int SZ_RED = KM * NW * 2 * TV;
+    constexpr int POOL = MM ? (SZ_B > SZ_RED ? SZ_B : SZ_RED) : SZ_B + SZ_RED;
+    __shared__ __attribute__((aligned(16))) float s_pool[POOL];
+    auto &s_k = *reinterpret_cast<float (*)[KM][D]>(s_pool);                   // token keys
+    auto &s_q = *reinterpret_cast<float (*)[KM][D]>(s_pool + SZ_K);            // token queries (receptances)
     // 2^{rho_t} k_t and 2^{rho_t} q_t (r_t), row r stored at (r % RPP) * R + r / RPP so
     // that the R rows of one thread (rs, rs + RPP, ...) are contiguous
-    __shared__ __attribute__((aligned(16))) float s_mv0[KM][D];
-    __shared__ __attribute__((aligned(16))) float s_mv1[KM][D];
+    auto &s_mv0 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 2 * SZ_K);
+    auto &s_mv1 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 3 * SZ_K);
+    auto &s_lg = *reinterpret_cast<float (*)[KM][GW]>(s_pool + 4 * SZ_K);        // log2 of each token's decay
+    auto &s_g = *reinterpret_cast<float (*)[KM + 1][GW]>(s_pool + 4 * SZ_K + SZ_LG);  // g_{t-1} at index t (g_{-1} = g_L)
+    auto &s_red = *reinterpret_cast<float (*)[KM][NW][2][TV]>(s_pool + (MM ? 0 : SZ_B));
     __shared__ __attribute__((aligned(16))) float s_scale[D];      // fold: 2^{g_{K-1}} per row
     __shared__ __attribute__((aligned(16))) float s_kt[CP * D];    // fold: decayed keys [entry][row]
-    __shared__ __attribute__((aligned(16))) float s_x[CP * TV];    // fold: value factors [entry][col]
+    // value factors [entry][col] for the fold.  In the matrix-core form rows
+    // L .. L+K-1 first hold the chunk's values (phase D reads v_t there and
+    // writes u_t in its place), and row CP takes the writes of token slots past
+    // the chunk.
+    __shared__ __attribute__((aligned(16))) float s_x[(CP + (MM ? 1 : 0)) * TV];
     __shared__ float s_coef[2][KM][CP];                            // per token, per entry
-    __shared__ __attribute__((aligned(16))) float s_red[KM][NW][2][TV];
     __shared__ float s_dot[KM];   // <k_t, q_t> or sum r u k
     __shared__ float s_beta[KM + 1];  // slot KM takes the writes of lanes that hold no token
 
@@ -163,6 +185,10 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         for (int j = 0; j < XR; ++j)
             xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * D);
     }
+    // the small loads above all go out before the tile's (loads complete in
+    // issue order, so one placed after the tile could only be used once the
+    // whole tile has arrived; the matrix-core form uses the values early)
+    if constexpr (MM) __builtin_amdgcn_sched_barrier(0);
     const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
     const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
     f4 s[R];
@@ -172,6 +198,14 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     // scheduled among them would wait for all loads issued before it)
     __builtin_amdgcn_sched_barrier(0);
     if (DELTA) s_beta[(c4 == 0 && ke < K) ? ke : KM] = beta_t;
+    // matrix-core form: the values go to LDS here so that they hold no registers
+    // through phases B and C, which brings it to five workgroups per CU (every
+    // wave writes the same values; no branch, so that no load is sunk past the
+    // tile)
+    if constexpr (MM) {
+#pragma unroll
+        for (int t = 0; t < KM; ++t) s_x[(t < K ? L + t : CP) * TV + tid % TV] = to_f32(vraw[t]);
+    }
 
     // ---------------- Phase B1: every token's inputs into LDS (group ke = token) ----------------
     const f4 kt_in = In4<TIn>::unpack(kraw);
@@ -346,6 +380,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) a[4 * i4 + c] = live ? v[c] : 0.f;
         }
+        // the products below are written over the scaled vectors
+        __syncthreads();
         m4 acc[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[c] = m4{0.f, 0.f, 0.f, 0.f};
@@ -429,7 +465,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
                 if (DELTA) yj += s_coef[0][t][L + m] * xs[m];
                 zj += s_coef[1][t][L + m] * xs[m];
             }
-            const float vj = to_f32(vraw[t]);
+            const float vj = MM ? s_x[(L + t) * TV + jt] : to_f32(vraw[t]);
             float xnew, o;
             if (DELTA) {
                 xnew = s_beta[t] * (vj - yj);
@@ -447,7 +483,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
                 if (DELTA)
                     static_cast<float *>(p.logX)[e * D + j] = xnew;
                 else
-                    static_cast<TIn *>(p.logX)[e * D + j] = vraw[t];
+                    store_raw(static_cast<TIn *>(p.logX) + e * D + j, vj);
             }
         }
     }

@@ -84,22 +84,27 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     // matrix-core form the per-wave products of phase C reuse their space (a
     // barrier separates the last read from the first write); the vector form
     // reads the scaled vectors while it writes products and keeps both.
+    // RWKV6 has no key-side products: no scaled keys, and one side of products
+    constexpr int NS = DELTA ? 2 : 1;          // sides of products: keys (delta rules), queries
+    constexpr int ZS = NS - 1;                 // index of the query side
     constexpr int SZ_K = KM * D;               // floats; every size a multiple of 4
+    constexpr int SZ_MV0 = DELTA ? SZ_K : 0;
     constexpr int SZ_LG = (KM * GW + 3) & ~3;
     constexpr int SZ_G = ((KM + 1) * GW + 3) & ~3;
-    constexpr int SZ_B = 4 * SZ_K + SZ_LG + SZ_G;
-    constexpr int SZ_RED = KM * NW * 2 * TV;
+    constexpr int SZ_B = 3 * SZ_K + SZ_MV0 + SZ_LG + SZ_G;
+    constexpr int SZ_RED = KM * NW * NS * TV;
     constexpr int POOL = MM ? (SZ_B > SZ_RED ? SZ_B : SZ_RED) : SZ_B + SZ_RED;
     __shared__ __attribute__((aligned(16))) float s_pool[POOL];
     auto &s_k = *reinterpret_cast<float (*)[KM][D]>(s_pool);                   // token keys
     auto &s_q = *reinterpret_cast<float (*)[KM][D]>(s_pool + SZ_K);            // token queries (receptances)
     // 2^{rho_t} k_t and 2^{rho_t} q_t (r_t), row r stored at (r % RPP) * R + r / RPP so
     // that the R rows of one thread (rs, rs + RPP, ...) are contiguous
-    auto &s_mv0 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 2 * SZ_K);
-    auto &s_mv1 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 3 * SZ_K);
-    auto &s_lg = *reinterpret_cast<float (*)[KM][GW]>(s_pool + 4 * SZ_K);        // log2 of each token's decay
-    auto &s_g = *reinterpret_cast<float (*)[KM + 1][GW]>(s_pool + 4 * SZ_K + SZ_LG);  // g_{t-1} at index t (g_{-1} = g_L)
-    auto &s_red = *reinterpret_cast<float (*)[KM][NW][2][TV]>(s_pool + (MM ? 0 : SZ_B));
+    // (s_mv0 is empty for RWKV6 and never read or written there)
+    auto &s_mv1 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 2 * SZ_K);
+    auto &s_mv0 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 3 * SZ_K);
+    auto &s_lg = *reinterpret_cast<float (*)[KM][GW]>(s_pool + 3 * SZ_K + SZ_MV0);  // log2 of each token's decay
+    auto &s_g = *reinterpret_cast<float (*)[KM + 1][GW]>(s_pool + 3 * SZ_K + SZ_MV0 + SZ_LG);  // g_{t-1} at index t (g_{-1} = g_L)
+    auto &s_red = *reinterpret_cast<float (*)[KM][NW][NS][TV]>(s_pool + (MM ? 0 : SZ_B));
     __shared__ __attribute__((aligned(16))) float s_scale[D];      // fold: 2^{g_{K-1}} per row
     __shared__ __attribute__((aligned(16))) float s_kt[CP * D];    // fold: decayed keys [entry][row]
     // value factors [entry][col] for the fold.  In the matrix-core form rows
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         for (int c = 0; c < 4; ++c) {
             const int row = c4 + c;
             const int at = (row % RPP) * R + row / RPP;
-            s_mv0[t][at] = m0[c];
+            if (DELTA) s_mv0[t][at] = m0[c];
             s_mv1[t][at] = m1[c];
         }
         if (!fold && tile == 0) {  // entry L + t of the log: the key copy and its log-decay
@@ -371,8 +376,9 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         const int m = lane & 15;
         const int kr = lane >> 4;
         const int side = m >> 3, tm = m & 7;
-        const bool live = tm < K;
-        const float *mv = side ? &s_mv1[tm][0] : &s_mv0[tm][0];
+        // RWKV6 has only the query side: its key-side vectors are zero
+        const bool live = tm < K && (DELTA || side == 1);
+        const float *mv = (side || !DELTA) ? &s_mv1[tm][0] : &s_mv0[tm][0];
         float a[R];
 #pragma unroll
         for (int i4 = 0; i4 < R / 4; ++i4) {
@@ -405,8 +411,9 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int mo = 4 * kr + q;
-            *reinterpret_cast<f4 *>(&s_red[mo & 7][wave][mo >> 3][4 * m]) =
-                f4{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
+            if (DELTA || (mo >> 3) == 1)
+                *reinterpret_cast<f4 *>(&s_red[mo & 7][wave][DELTA ? (mo >> 3) : 0][4 * m]) =
+                    f4{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
         }
     } else {
 #pragma unroll
@@ -415,7 +422,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i4 = 0; i4 < R / 4; ++i4) {
-                const f4 a = *reinterpret_cast<const f4 *>(&s_mv0[t][rs * R + 4 * i4]);
+                const f4 a = DELTA ? *reinterpret_cast<const f4 *>(&s_mv0[t][rs * R + 4 * i4]) : f4{0.f, 0.f, 0.f, 0.f};
                 const f4 b = *reinterpret_cast<const f4 *>(&s_mv1[t][rs * R + 4 * i4]);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
@@ -439,7 +446,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             }
             if (lane < LPR) {
                 if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][wave][0][4 * cg]) = y;
-                *reinterpret_cast<f4 *>(&s_red[t][wave][1][4 * cg]) = z;
+                *reinterpret_cast<f4 *>(&s_red[t][wave][ZS][4 * cg]) = z;
             }
         }
     }
@@ -457,7 +464,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
             for (int w = 0; w < NW; ++w) {
                 if (DELTA) yj += s_red[t][w][0][jt];
-                zj += s_red[t][w][1][jt];
+                zj += s_red[t][w][ZS][jt];
             }
 #pragma unroll
             for (int m = 0; m < KM; ++m) {

@@ -24,6 +24,12 @@
 
 namespace dlk {
 
+// The input-dtype bits of a value that was read from that dtype (exact).
+__device__ __forceinline__ void store_raw(float *dst, float x) { *dst = x; }
+__device__ __forceinline__ void store_raw(bf16_bits *dst, float x) {
+    *dst = static_cast<bf16_bits>(__float_as_uint(x) >> 16);
+}
+
 // Token pointers of the kernel arguments as opaque scalar values.  The lanes
 // of one wave belong to GPW consecutive key-side groups (tokens t0 .. t0 +
 // GPW - 1, t0 uniform), so each lane chooses among GPW pointers, each a
@@ -31,12 +37,6 @@ namespace dlk {
 // back into an index into the argument array, read with a vector load that
 // the data load must wait for; the empty asm prevents that.  The result is
 // returned as a global-memory pointer (the asm hides where it came from).
-// The input-dtype bits of a value that was read from that dtype (exact).
-__device__ __forceinline__ void store_raw(float *dst, float x) { *dst = x; }
-__device__ __forceinline__ void store_raw(bf16_bits *dst, float x) {
-    *dst = static_cast<bf16_bits>(__float_as_uint(x) >> 16);
-}
-
 template <typename T>
 __device__ __forceinline__ T opaque_scalar(T x) {
     asm volatile("" : "+s"(x));

@@ -323,20 +323,27 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             if (t < K && (is_old || (is_new && e - L < t))) {
                 const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
                 const f4 kt = ke4 * exp2v(rho - ge4);
-                pk[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_k[t][c4]));
+                if (DELTA) pk[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_k[t][c4]));
                 pq[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_q[t][c4]));
             }
         }
+        // in batches of four tokens, so that the independent exchanges of a
+        // batch interleave; the second batch only when the chunk reaches it
+        // (RWKV6 needs no key-side coefficients)
 #pragma unroll
-        for (int t = 0; t < KM; ++t) {
-            pk[t] = group_sum_valu<KL>(pk[t]);
-            pq[t] = group_sum_valu<KL>(pq[t]);
+        for (int h = 0; h < KM; h += 4) {
+            if (h > 0 && K <= h) break;
+#pragma unroll
+            for (int t = h; t < h + 4; ++t) {
+                if (DELTA) pk[t] = group_sum_valu<KL>(pk[t]);
+                pq[t] = group_sum_valu<KL>(pq[t]);
+            }
         }
         if (c4 == 0 && e < NE) {
 #pragma unroll
             for (int t = 0; t < KM; ++t) {
                 if (t < K) {
-                    s_coef[0][t][e] = pk[t];
+                    if (DELTA) s_coef[0][t][e] = pk[t];
                     s_coef[1][t][e] = pq[t];
                 }
             }

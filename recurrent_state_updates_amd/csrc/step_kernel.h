@@ -123,15 +123,22 @@ struct Geom {
 };
 
 // Tile shape of the single-token kernels: one workgroup per head at every
-// width -- 64 KB and 512 threads at D = 128, 16 KB and 128 threads at D = 64,
-// 4 KB and 64 threads at D = 32 -- eight float4 of the state per thread.  A
-// whole head is one contiguous block, which streams about 7 % faster on
-// MI355X than two 64-column halves of it (rows read as 256-byte pieces at a
-// 512-byte stride), for the append and the fold alike.
-template <int D>
+// width -- 64 KB at D = 128, 16 KB and 128 threads at D = 64, 4 KB and 64
+// threads at D = 32.  A whole head is one contiguous block, which streams
+// about 7 % faster on MI355X than two 64-column halves of it (rows read as
+// 256-byte pieces at a 512-byte stride), for the append and the fold alike.
+// At D = 128 the decode modes use 256 threads of sixteen float4 each: four
+// heads per CU instead of three, appends 2-4 % faster than with 512 threads
+// of eight.  The decode-and-fold keeps the append's shape, so that per-slot
+// decode (one kernel that appends or folds per slot) adds its column sums in
+// the same order as the lockstep kernels and gives the same bits.  The
+// standalone fold and the eager kernel keep 512 threads, 1-2 % faster for
+// them; the fold's result does not depend on the shape (no column sums).
+template <int D, int MODE>
 struct Shape {
+    static constexpr bool WIDE = MODE == MODE_FOLD || MODE == MODE_EAGER;
     static constexpr int TV = D;
-    static constexpr int NT = D == 128 ? 512 : (D == 64 ? 128 : 64);
+    static constexpr int NT = D == 128 ? (WIDE ? 512 : 256) : (D == 64 ? 128 : 64);
 };
 
 // Workgroups are handed to the eight XCDs round-robin in dispatch order

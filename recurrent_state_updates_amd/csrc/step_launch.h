@@ -9,7 +9,7 @@ namespace dlk {
 
 template <int OP, typename TIn, int D, int MODE, int CMAX>
 hipError_t launch_one(const StepParams &p, hipStream_t s) {
-    constexpr int TV = Shape<D>::TV, NT = Shape<D>::NT;
+    constexpr int TV = Shape<D, MODE>::TV, NT = Shape<D, MODE>::NT;
     const unsigned blocks = (unsigned)p.N * (MODE == MODE_PREP ? 1 : D / TV);
     hipLaunchKernelGGL((step_kernel<OP, TIn, D, TV, NT, MODE, CMAX>), dim3(blocks), dim3(NT), 0, s, p);
     return hipGetLastError();

@@ -264,7 +264,7 @@ dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *
  * (gist.science summary, "Modello di Traffico": appends of compact factors,
  * one amortised dense write per interval, replay of the log).  Bandwidths
  * <= 0 select the values fitted to these kernels' measured times on MI355X
- * (6075 GB/s for appends, 5725 GB/s for the fold; within 3 % of the measured
+ * (6250 GB/s for appends, 5675 GB/s for the fold; within 2 % of the measured
  * amortised time for C = 1..32 at GDN and KDA B=128 d=128, launch gaps
  * included).  Host-only.  Returns a negative value for an
  * invalid cfg. */

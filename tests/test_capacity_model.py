@@ -23,7 +23,7 @@ def test_library_model_matches_the_python_byte_model(op, d, C):
 
 def test_default_bandwidths_and_argmin():
     cfg = dl.make_config("gdn", "bf16", 128, 32, 128, 128, 8)
-    assert dl.dl_predict_token_us(cfg) == pytest.approx(_predict_py("gdn", 128, 32, 128, 8, 6075, 5725))
+    assert dl.dl_predict_token_us(cfg) == pytest.approx(_predict_py("gdn", 128, 32, 128, 8, 6250, 5675))
     for max_c in (1, 4, 8, 32):
         best = dl.dl_choose_capacity(cfg, max_c)
         preds = {C: dl.dl_predict_token_us(dl.make_config("gdn", "bf16", 128, 32, 128, 128, C))

@@ -28,8 +28,12 @@
  *    reused or freed once the stream has passed the call.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *  - State buffers (base, dst, state) and the workspace must be 16-byte
- *    aligned; every other device pointer must be aligned to its element
- *    size.  Buffers named as outputs must not overlap inputs unless stated.
+ *    aligned.  The kernels read q and k four channels at a time, so those
+ *    must be aligned to four elements (8 bytes in bf16, 16 in f32), and the
+ *    per-channel decay (KDA, RWKV6) and the bonus as float4, so those must
+ *    be 16-byte aligned; every other device pointer must be aligned to its
+ *    element size.  Buffers named as outputs must not overlap inputs unless
+ *    stated.
  *  - Return values are dl_status codes: DL_OK (0) or a negative error.  Every
  *    argument is checked before anything is enqueued, so on any error but
  *    DL_ERR_HIP nothing was enqueued and the handle is unchanged;

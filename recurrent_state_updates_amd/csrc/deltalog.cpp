@@ -119,14 +119,17 @@ dl_status check_args(const dl_config *cfg, const dl_step_args *a) {
         if (a->bonus) return fail(DL_ERR_ARG, "args->bonus must be NULL for GDN and KDA");
     }
     const size_t es = in_size(cfg->in_dtype);
-    const void *in_ptrs[] = {a->q, a->k, a->v};
-    for (const void *p : in_ptrs)
-        if (reinterpret_cast<uintptr_t>(p) % es != 0)
-            return fail(DL_ERR_ARG, "q, k and v must be aligned to their element size");
-    const void *f32_ptrs[] = {a->beta, a->decay, a->bonus, a->out};
+    auto addr = [](const void *p) { return reinterpret_cast<uintptr_t>(p); };
+    // the kernels read q and k four channels at a time (one 8- or 16-byte
+    // load), and the per-channel decays and the bonus as float4
+    if (addr(a->q) % (4 * es) != 0 || addr(a->k) % (4 * es) != 0)
+        return fail(DL_ERR_ARG, "q and k must be aligned to four elements (8 bytes in bf16, 16 in f32)");
+    if (addr(a->v) % es != 0) return fail(DL_ERR_ARG, "v must be aligned to its element size");
+    if ((cfg->op != DL_GDN && addr(a->decay) % 16 != 0) || addr(a->bonus) % 16 != 0)
+        return fail(DL_ERR_ARG, "the per-channel decay and the bonus must be 16-byte aligned");
+    const void *f32_ptrs[] = {a->beta, a->decay, a->out};
     for (const void *p : f32_ptrs)
-        if (reinterpret_cast<uintptr_t>(p) % 4 != 0)
-            return fail(DL_ERR_ARG, "beta, decay, bonus and out must be 4-byte aligned");
+        if (addr(p) % 4 != 0) return fail(DL_ERR_ARG, "beta, decay and out must be 4-byte aligned");
     return DL_OK;
 }
 

@@ -134,6 +134,9 @@ def _args(**over):
     ("rwkv6", dict()),  # beta given, bonus missing
     ("rwkv6", dict(beta=0)),  # bonus missing
     ("gdn", dict(k=FAKE + 0x101)), ("gdn", dict(out=FAKE + 0x502)), ("gdn", dict(beta=FAKE + 0x302)),
+    # q and k are read four channels at a time, per-channel decays and the bonus as float4
+    ("gdn", dict(q=FAKE + 2)), ("kda", dict(k=FAKE + 0x104)), ("gdn", dict(v=FAKE + 0x201)),
+    ("kda", dict(decay=FAKE + 0x404)), ("rwkv6", dict(beta=0, bonus=FAKE + 0x608)),
 ])
 def test_decode_step_rejects_bad_args_without_state_change(op, over):
     cfg = dl.make_config(op, "bf16", 2, 4, 64, 64, 4)

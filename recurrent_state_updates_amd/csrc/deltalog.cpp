@@ -352,6 +352,10 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     if (K < 1 || K > DL_MAX_TOKENS) return fail(DL_ERR_SHAPE, "K must lie in [1, 8]");
     for (int t = 0; t < K; ++t)
         if ((st = check_args(&h->cfg, &args[t])) != DL_OK) return st;
+    // the bonus is a per-head parameter: one launch takes it from the first token
+    for (int t = 1; t < K; ++t)
+        if (args[t].bonus != args[0].bonus)
+            return fail(DL_ERR_ARG, "every token of a call must carry the same bonus");
     if (h->slots) {
         // every slot's log fills at its own token: one per-slot step per token
         for (int t = 0; t < K; ++t)

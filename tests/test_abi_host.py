@@ -169,6 +169,18 @@ def test_decode_tokens_validates_before_launching():
         assert dl.dl_log_length(h) == 0
     finally:
         dl.dl_state_destroy(h)
+    # RWKV6: one bonus for all tokens of a call
+    cfg = dl.make_config("rwkv6", "bf16", 2, 4, 64, 64, 4)
+    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    try:
+        a0, a1 = _args(beta=0, bonus=FAKE + 0x600), _args(beta=0, bonus=FAKE + 0x700)
+        with pytest.raises(dl.DeltaLogError) as ei:
+            dl.dl_decode_tokens(h, [a0, a1])
+        assert ei.value.status == B.DL_ERR_ARG
+        assert "bonus" in dl.dl_last_error()
+        assert dl.dl_log_length(h) == 0
+    finally:
+        dl.dl_state_destroy(h)
 
 
 def test_slot_calls_validate_on_the_host():

@@ -265,9 +265,12 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     const int C = p.C;
     int L = LOGGED ? p.L : 0;
     if (LOGGED && p.slot_base != nullptr) {
-        // per-slot logs: this slot's own length; a decode step launches the
-        // append for slots that stay below C and the fold for slots that fill
-        // (the whole workgroup leaves together, before any barrier)
+        // per-slot logs: this slot's own length.  A per-slot decode step is
+        // one AUTO launch (append, or fold when this token fills the slot's
+        // log) and a per-slot merge or materialise a FOLD launch; APPEND and
+        // MERGE, given slot arrays, serve only the slots that stay below C or
+        // fill, respectively.  The whole workgroup leaves together, before
+        // any barrier.
         const int b = n / p.H;
         if (!p.slot_active[b]) return;
         L = (int)((p.step - (unsigned)p.slot_base[b]) % (unsigned)C);

@@ -114,6 +114,9 @@ class DeltaLogState:
         """Decode K tokens in one call (dl_decode_tokens).  q, k, v, beta, decay
         carry a leading token axis [K, ...]; returns out [K, B, H, dv] fp32."""
         K = q.shape[0]
+        for name, t in (("k", k), ("v", v), ("beta", beta), ("decay", decay), ("out", out)):
+            if t is not None and t.shape[0] != K:
+                raise ValueError(f"{name} carries {t.shape[0]} tokens, q carries {K}")
         if out is None:
             out = torch.empty((K, self.B, self.H, self.dv), dtype=torch.float32, device=self.device)
         args = [make_step_args(self.op, self.in_dtype, self.B, self.H, self.dk, self.dv, self.device,

@@ -77,14 +77,45 @@ def test_chunks_match_oracle(op, dtype, d, C, sizes):
     assert max(gs.rel(outs[t].cpu(), single[t].cpu()) for t in range(T)) <= 1e-5
 
 
-def test_full_size_chunk_of_four():
-    w = workloads.WORKLOADS["gdn_b128_h32_d128"]
-    x = workloads.generate_workload(w, T=32)
+FULL_CASES = [("gdn_b128_h32_d128", "gdn", (4,)), ("gdn_b128_h32_d128", "gdn", (8,)),
+              ("kda_b128_h32_d128", "kda", (8,)), ("rwkv6_b128_h32_d64", "rwkv6", (8,)),
+              ("kda_b128_h32_d128", "kda", (5, 7)), ("rwkv6_b128_h32_d64", "rwkv6", (3, 6))]
+
+
+@pytest.mark.parametrize("name,op,sizes", FULL_CASES)
+def test_full_size_chunks(name, op, sizes):
+    """Serving shape, C=8, in the launch configuration the multi-token bench times:
+    every output of 64 sampled heads over 32 tokens, and their state at two
+    chunk boundaries (one mid-cycle for the uneven schedules)."""
+    w = workloads.WORKLOADS[name]
+    T = 32
+    x = workloads.generate_workload(w, T=T)
     dev = gs.to_device(x, DEV)
+    bounds, t, i = [], 0, 0
+    while t < T:
+        t += min(sizes[i % len(sizes)], T - t)
+        i += 1
+        bounds.append(t)
+    chk = sorted({bounds[len(bounds) // 2 - 1], T})
     heads = gs.head_sample(w.heads, 64, seed=3)
-    ref = gs.oracle_run(x, "gdn", heads=heads, chk_steps=[32], nthreads=16)
-    outs, states, _ = run_chunks(dev, "gdn", "bf16", 8, (4,), state_steps={32})
+    ref = gs.oracle_run(x, op, heads=heads, chk_steps=chk, nthreads=16)
+    outs, states, _ = run_chunks(dev, op, w.in_dtype, 8, sizes, state_steps=set(chk))
     hs = torch.as_tensor(heads, dtype=torch.long, device=outs.device)
-    o = outs.view(32, w.heads, w.d)[:, hs].cpu().numpy()
-    assert max(gs.rel(o[t], ref["out"][t]) for t in range(32)) <= gs.OUT_GATE
-    assert gs.rel(states[32].numpy()[heads], ref["states"][0]) <= gs.STATE_GATE
+    o = outs.view(T, w.heads, w.d)[:, hs].cpu().numpy()
+    assert max(gs.rel(o[t], ref["out"][t]) for t in range(T)) <= gs.OUT_GATE
+    for m, b in enumerate(chk):
+        assert gs.rel(states[b].numpy()[heads], ref["states"][m]) <= gs.STATE_GATE, b
+
+
+def test_token_axes_must_agree():
+    """The torch front end rejects a chunk whose inputs carry different token counts
+    before anything reaches the library."""
+    x = workloads.generate("gdn", 1, 2, 32, 32, 4, "f32", seed=7)
+    dev = gs.to_device(x, DEV)
+    st = dl.DeltaLogState("gdn", "f32", dev["S0"].clone(), 4)
+    c = _chunk(dev, 0, 3)
+    c["v"] = dev["v"][0:2]
+    with pytest.raises(ValueError, match="v carries 2 tokens"):
+        st.step_tokens(**c)
+    assert st.log_length == 0
+    st.close()

@@ -56,7 +56,9 @@
  *                  fp32, every value in (0, 1] (0 is undefined behaviour)
  *    bonus         [H, dk]        fp32   (RWKV6 per-head bonus u)
  *    out           [B, H, dv]     fp32
- * Supported shapes: dk == dv in {32, 64, 128}; 1 <= C <= DL_MAX_CAPACITY.
+ * Supported shapes: dk == dv in {32, 64, 128}; 1 <= C <= DL_MAX_CAPACITY;
+ * B*H <= DL_MAX_HEADS (a launch holds at most 2^32 work-items and the widest
+ * kernel runs 512 per head; at dk = 128 that bound is a 550 GB state).
  */
 #ifndef DELTALOG_H
 #define DELTALOG_H
@@ -69,6 +71,7 @@ extern "C" {
 
 #define DL_MAX_CAPACITY 32
 #define DL_MAX_TOKENS 8
+#define DL_MAX_HEADS (1 << 23)
 
 typedef enum { DL_GDN = 0, DL_KDA = 1, DL_RWKV6 = 2 } dl_op;
 typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;

@@ -8,7 +8,7 @@ work runs in hand-written HIP kernels for gfx950 behind the C ABI of
 ``include/deltalog.h``; this package is its Python binding.
 """
 from ._binding import (  # noqa: F401
-    DL_BF16, DL_F32, DL_GDN, DL_KDA, DL_MAX_CAPACITY, DL_MAX_TOKENS, DL_RWKV6, Config, DeltaLogError, StepArgs,
+    DL_BF16, DL_F32, DL_GDN, DL_KDA, DL_MAX_CAPACITY, DL_MAX_HEADS, DL_MAX_TOKENS, DL_RWKV6, Config, DeltaLogError, StepArgs,
     dl_choose_capacity, dl_decode_step, dl_decode_tokens, dl_eager_step, dl_graph_capture_cycle,
     dl_graph_destroy, dl_graph_launch, dl_last_error, dl_log_length, dl_materialize, dl_materialize_slot, dl_merge,
     dl_predict_token_us, dl_prep_bytes, dl_set_split_replay, dl_slot_activate, dl_slot_deactivate,

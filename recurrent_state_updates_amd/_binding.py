@@ -19,6 +19,7 @@ DL_OK = 0
 DL_ERR_ARG, DL_ERR_SHAPE, DL_ERR_UNSUPPORTED, DL_ERR_HIP, DL_ERR_WORKSPACE = -1, -2, -3, -4, -5
 DL_MAX_CAPACITY = 32
 DL_MAX_TOKENS = 8
+DL_MAX_HEADS = 1 << 23
 
 OP_CODES = {"gdn": DL_GDN, "kda": DL_KDA, "rwkv6": DL_RWKV6}
 DTYPE_CODES = {"f32": DL_F32, "bf16": DL_BF16}

@@ -18,7 +18,6 @@
 #include <stdio.h>
 
 #include <algorithm>
-#include <limits>
 #include <new>
 #include <string>
 #include <vector>
@@ -81,10 +80,8 @@ dl_status check_config(const dl_config *cfg, size_t *heads) {
     if (cfg->dk != 32 && cfg->dk != 64 && cfg->dk != 128)
         return fail(DL_ERR_UNSUPPORTED, "dk must be 32, 64 or 128");
     const size_t n = (size_t)cfg->B * (size_t)cfg->H;
-    // grid.x is an int; the largest array is N * C * D * 4 bytes
-    if (n > (size_t)std::numeric_limits<int>::max() ||
-        n > std::numeric_limits<size_t>::max() / ((size_t)DL_MAX_CAPACITY * 128 * 128 * 4))
-        return fail(DL_ERR_SHAPE, "B * H is too large");
+    // a launch holds at most 2^32 work-items and the widest kernel runs 512 per head
+    if (n > (size_t)DL_MAX_HEADS) return fail(DL_ERR_SHAPE, "B * H exceeds DL_MAX_HEADS");
     *heads = n;
     return DL_OK;
 }

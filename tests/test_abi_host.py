@@ -77,8 +77,10 @@ def test_workspace_size_and_layout(op, dtype, d, C):
     (dict(B=0), B.DL_ERR_SHAPE), (dict(H=-1), B.DL_ERR_SHAPE),
     (dict(C=0), B.DL_ERR_SHAPE), (dict(C=33), B.DL_ERR_SHAPE),
     (dict(dk=128, dv=64), B.DL_ERR_UNSUPPORTED), (dict(dk=96, dv=96), B.DL_ERR_UNSUPPORTED),
+    (dict(B=(1 << 22) + 1, H=2, dk=32, dv=32), B.DL_ERR_SHAPE), (dict(B=1 << 30, H=1 << 30), B.DL_ERR_SHAPE),
 ])
 def test_invalid_configs(kw, code):
+    """Every bad config fails at size query and at init, with the status and a reason."""
     base = dict(op=0, in_dtype=1, B=2, H=2, dk=64, dv=64, C=4)
     base.update(kw)
     cfg = B.Config(**base)
@@ -270,3 +272,10 @@ def test_library_is_built_for_gfx950():
     with open(B.LIB_PATH, "rb") as f:
         blob = f.read()
     assert b"gfx950" in blob
+
+
+def test_largest_head_count_is_accepted():
+    cfg = B.Config(op=0, in_dtype=1, B=1 << 21, H=4, dk=32, dv=32, C=32)
+    assert B.DL_MAX_HEADS == 1 << 23
+    # X (fp32) and K (bf16) for 32 entries of width 32 per head, plus the decays
+    assert dl.dl_workspace_bytes(cfg) > (1 << 23) * 32 * 32 * (4 + 2)

@@ -57,8 +57,12 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
     return (global_ptr<E>)static_cast<const E *>(r);
 }
 
-// MM selects the matrix-core form of the token products (phase C); it needs
-// 16 lanes per tile row and pays off from about three tokens on.
+// MM selects the matrix-core form of the token products (phase C); it pays
+// off from about three tokens on.  Its 16x16x4 k-steps are four rows of 64
+// columns, 16 lanes per (row, column range).  With TV = D = 128 it takes whole
+// heads: waves 2h and 2h + 1 hold column half h, rows 0-63 and 64-127, so a
+// head streams as one contiguous 64 KB block, its key-side work is done once,
+// and two waves' products add up per column.
 template <int OP, typename TIn, int D, int TV, int NT, int CMAX, bool MM>
 __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     using G = Geom<D, TV, NT>;
@@ -69,7 +73,13 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     constexpr int KM = KMAX_TOKENS;
     constexpr int CP = CMAX;  // entry slots: old entries plus the chunk's tokens (<= C <= CMAX)
     constexpr int KPASS = (CMAX + EPP - 1) / EPP;
-    constexpr int XR = (CMAX + RPP - 1) / RPP;
+    constexpr bool WH = MM && TV == D;  // whole heads on the matrix cores
+    static_assert(!WH || (D == 128 && NT == 256), "whole-head matrix-core form: D = 128, 256 threads");
+    // s[i] holds tile row rbase + RSTEP * i; xrow[j] holds log entry ebase + ESTEP * j
+    constexpr int RSTEP = WH ? 4 : RPP;
+    constexpr int ESTEP = WH ? 8 : RPP;
+    constexpr int NWR = WH ? 2 : NW;  // row blocks whose products add up in each column
+    constexpr int XR = (CMAX + ESTEP - 1) / ESTEP;
     constexpr int GW = GDN ? 1 : D;  // log-decay values per entry
     using TX = typename std::conditional<DELTA, float, TIn>::type;
     using Raw = typename In4<TIn>::raw;
@@ -92,19 +102,19 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     constexpr int SZ_LG = (KM * GW + 3) & ~3;
     constexpr int SZ_G = ((KM + 1) * GW + 3) & ~3;
     constexpr int SZ_B = 3 * SZ_K + SZ_MV0 + SZ_LG + SZ_G;
-    constexpr int SZ_RED = KM * NW * NS * TV;
+    constexpr int SZ_RED = KM * NWR * NS * TV;
     constexpr int POOL = MM ? (SZ_B > SZ_RED ? SZ_B : SZ_RED) : SZ_B + SZ_RED;
     __shared__ __attribute__((aligned(16))) float s_pool[POOL];
     auto &s_k = *reinterpret_cast<float (*)[KM][D]>(s_pool);                   // token keys
     auto &s_q = *reinterpret_cast<float (*)[KM][D]>(s_pool + SZ_K);            // token queries (receptances)
-    // 2^{rho_t} k_t and 2^{rho_t} q_t (r_t), row r stored at (r % RPP) * R + r / RPP so
-    // that the R rows of one thread (rs, rs + RPP, ...) are contiguous
+    // 2^{rho_t} k_t and 2^{rho_t} q_t (r_t), row r stored at mv_at(r) so that the R
+    // rows of one thread (rbase, rbase + RSTEP, ...) are contiguous
     // (s_mv0 is empty for RWKV6 and never read or written there)
     auto &s_mv1 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 2 * SZ_K);
     auto &s_mv0 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 3 * SZ_K);
     auto &s_lg = *reinterpret_cast<float (*)[KM][GW]>(s_pool + 3 * SZ_K + SZ_MV0);  // log2 of each token's decay
     auto &s_g = *reinterpret_cast<float (*)[KM + 1][GW]>(s_pool + 3 * SZ_K + SZ_MV0 + SZ_LG);  // g_{t-1} at index t (g_{-1} = g_L)
-    auto &s_red = *reinterpret_cast<float (*)[KM][NW][NS][TV]>(s_pool + (MM ? 0 : SZ_B));
+    auto &s_red = *reinterpret_cast<float (*)[KM][NWR][NS][TV]>(s_pool + (MM ? 0 : SZ_B));
     __shared__ __attribute__((aligned(16))) float s_scale[D];      // fold: 2^{g_{K-1}} per row
     __shared__ __attribute__((aligned(16))) float s_kt[CP * D];    // fold: decayed keys [entry][row]
     // value factors [entry][col] for the fold.  In the matrix-core form rows
@@ -127,8 +137,13 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     const bool fold = p.fold != 0;
     const int NE = L + K;               // entries after the chunk
     const int last = L > 0 ? L - 1 : 0;
-    const int cg = tid % LPR;
-    const int rs = tid / LPR;
+    // the thread's rows of the tile, its four columns (from cq, within the
+    // tile) and its rows of the old log's value factors
+    const int rbase = WH ? 64 * (wave & 1) + (lane >> 4) : tid / LPR;
+    const int cq = WH ? 64 * (wave >> 1) + 4 * (lane & 15) : 4 * (tid % LPR);
+    const int ebase = WH ? 4 * (wave & 1) + (lane >> 4) : tid / LPR;
+    const int rblk = WH ? (wave & 1) : wave;
+    auto mv_at = [](int row) { return (row % RSTEP) * (D / RSTEP) + row / RSTEP; };
     const int col0 = tile * TV;
     const int c4 = 4 * (tid % KL);
     const int ke = tid / KL;            // key-side group: token ke, then entries ps*EPP + ke
@@ -185,20 +200,20 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             else
                 glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * D + c4);
         }
-        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0 + 4 * cg;
+        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0 + cq;
 #pragma unroll
         for (int j = 0; j < XR; ++j)
-            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * D);
+            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(ebase + ESTEP * j, last) * D);
     }
     // the small loads above all go out before the tile's (loads complete in
     // issue order, so one placed after the tile could only be used once the
     // whole tile has arrived; the matrix-core form uses the values early)
     if constexpr (MM) __builtin_amdgcn_sched_barrier(0);
-    const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
+    const size_t tile4 = (size_t)n * (D * D / 4) + (col0 + cq) / 4 + (size_t)rbase * (D / 4);
     const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
     f4 s[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
+    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RSTEP * (D / 4));
     // every load above is issued before anything consumes one (a consumer
     // scheduled among them would wait for all loads issued before it)
     __builtin_amdgcn_sched_barrier(0);
@@ -279,8 +294,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         const f4 m0 = sc * kt_in, m1 = sc * qt_in;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const int row = c4 + c;
-            const int at = (row % RPP) * R + row / RPP;
+            const int at = mv_at(c4 + c);
             if (DELTA) s_mv0[t][at] = m0[c];
             s_mv1[t][at] = m1[c];
         }
@@ -355,8 +369,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         // old value factors of the tile for the fold; zero the slots up to a multiple of four
 #pragma unroll
         for (int j = 0; j < XR; ++j) {
-            const int i = rs + RPP * j;
-            if (i < L) *reinterpret_cast<f4 *>(&s_x[i * TV + 4 * cg]) = In4<TX>::unpack(xrow[j]);
+            const int i = ebase + ESTEP * j;
+            if (i < L) *reinterpret_cast<f4 *>(&s_x[i * TV + cq]) = In4<TX>::unpack(xrow[j]);
         }
         const int pad = ((NE + 3) & ~3) - NE;
         for (int idx = tid; idx < pad * D; idx += NT) {
@@ -369,13 +383,14 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     __syncthreads();
 
     // ---------------- Phase C: base products of every token from the register tile ----------------
-    static_assert(!MM || (LPR == 16 && 2 * KM == 16), "matrix-core form: 16 lanes per row, 16 vectors");
+    static_assert(!MM || ((WH || LPR == 16) && 2 * KM == 16), "matrix-core form: 16 lanes per row, 16 vectors");
     if constexpr (MM) {
         // On the matrix cores: P[m][col] = sum_row A[m][row] S[row][col] over this
         // wave's rows, with the 16 vectors m = (side, token) = (m / 8, m % 8):
         // side 0 the scaled keys, side 1 the scaled queries (receptances).  The
         // register tile already has the 16x16x4 operand layout: in k-step i,
-        // lane l holds row 4 wave + l/16 + RPP i and columns 4 (l % 16) + c, so
+        // lane l holds row rbase + RSTEP i (rbase = its wave's first row + l/16)
+        // and columns cq + c (cq = its wave's first column + 4 (l % 16)), so
         // component c of s[i] is the B operand of the c-th product, and lane l
         // supplies A[l % 16][that row].  The old log joins as XR more k-steps
         // with the replay coefficients as A and the logged value rows as B.
@@ -389,7 +404,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
         float a[R];
 #pragma unroll
         for (int i4 = 0; i4 < R / 4; ++i4) {
-            const f4 v = *reinterpret_cast<const f4 *>(&mv[(4 * wave + kr) * R + 4 * i4]);
+            const f4 v = *reinterpret_cast<const f4 *>(&mv[mv_at(rbase) + 4 * i4]);
 #pragma unroll
             for (int c = 0; c < 4; ++c) a[4 * i4 + c] = live ? v[c] : 0.f;
         }
@@ -408,18 +423,18 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             // entries at or past L were loaded from a clamped index and may be
             // anything (an unused slot holds whatever the workspace held): zero
             // both operands, since 0 * NaN would poison the sum
-            const int e = rs + RPP * j;  // rs = 4 wave + kr
+            const int e = ebase + ESTEP * j;
             const float co = (live && e < L) ? s_coef[side][tm][e] : 0.f;
             const f4 xv = e < L ? In4<TX>::unpack(xrow[j]) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(co, xv[c], acc[c], 0, 0, 0);
         }
-        // lane l holds P[4 (l / 16) + q][4 (l % 16) + c] in acc[c][q]
+        // lane l holds P[4 (l / 16) + q][cq + c] in acc[c][q]
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int mo = 4 * kr + q;
             if (DELTA || (mo >> 3) == 1)
-                *reinterpret_cast<f4 *>(&s_red[mo & 7][wave][DELTA ? (mo >> 3) : 0][4 * m]) =
+                *reinterpret_cast<f4 *>(&s_red[mo & 7][rblk][DELTA ? (mo >> 3) : 0][cq]) =
                     f4{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
         }
     } else {
@@ -429,8 +444,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int i4 = 0; i4 < R / 4; ++i4) {
-                const f4 a = DELTA ? *reinterpret_cast<const f4 *>(&s_mv0[t][rs * R + 4 * i4]) : f4{0.f, 0.f, 0.f, 0.f};
-                const f4 b = *reinterpret_cast<const f4 *>(&s_mv1[t][rs * R + 4 * i4]);
+                const f4 a = DELTA ? *reinterpret_cast<const f4 *>(&s_mv0[t][mv_at(rbase) + 4 * i4]) : f4{0.f, 0.f, 0.f, 0.f};
+                const f4 b = *reinterpret_cast<const f4 *>(&s_mv1[t][mv_at(rbase) + 4 * i4]);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if (DELTA) y += s[4 * i4 + c] * a[c];
@@ -439,7 +454,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             }
 #pragma unroll
             for (int j = 0; j < XR; ++j) {
-                const int i = rs + RPP * j;
+                const int i = ebase + ESTEP * j;
                 if (i < L) {
                     const f4 x = In4<TX>::unpack(xrow[j]);
                     if (DELTA) y += s_coef[0][t][i] * x;
@@ -452,8 +467,8 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
                 z[c] = column_sum_valu<LPR>(z[c]);
             }
             if (lane < LPR) {
-                if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][wave][0][4 * cg]) = y;
-                *reinterpret_cast<f4 *>(&s_red[t][wave][ZS][4 * cg]) = z;
+                if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][rblk][0][cq]) = y;
+                *reinterpret_cast<f4 *>(&s_red[t][rblk][ZS][cq]) = z;
             }
         }
     }
@@ -469,7 +484,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             if (t >= K) break;
             float yj = 0.f, zj = 0.f;
 #pragma unroll
-            for (int w = 0; w < NW; ++w) {
+            for (int w = 0; w < NWR; ++w) {
                 if (DELTA) yj += s_red[t][w][0][jt];
                 zj += s_red[t][w][ZS][jt];
             }
@@ -505,80 +520,87 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     // ---------------- Phase E: fold every entry into the base when the chunk fills the log ----------------
     if (fold) {
         __syncthreads();
-        f4 acc[R];
-#pragma unroll
-        for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rs + RPP * i];
+        f4 *dst4 = reinterpret_cast<f4 *>(p.base) + tile4;
         if constexpr (MM) {
             // The rank-NE update on the matrix cores.  For row group g and
-            // column offset c: P[M][n] = sum_e kt[e][row(M)] x[e][4 n + c] with
-            // row(M) = 4 wave + M / 4 + RPP (4 g + M % 4), so that lane l ends
-            // with P[4 (l / 16) + q][l % 16] = the update of its own s[4 g + q][c].
+            // column offset c: P[M][n] = sum_e kt[e][row(M)] x[e][4 n + c] (columns
+            // from the wave's first) with row(M) = the wave's first row + M / 4 +
+            // RSTEP (4 g + M % 4), so that lane l ends with P[4 (l / 16) + q][l % 16]
+            // = the update of its own s[4 g + q][c].  Each group's rows are stored
+            // as soon as they are done, so that one group's products are live at
+            // a time.
             // The entry slots past NE are zero up to a multiple of four.
             typedef float m4 __attribute__((ext_vector_type(4)));
             const int m = lane & 15, kr = lane >> 4;
 #pragma unroll
             for (int g = 0; g < R / 4; ++g) {
-                const int arow = 4 * wave + (m >> 2) + RPP * (4 * g + (m & 3));
+                const int arow = rbase - kr + (m >> 2) + RSTEP * (4 * g + (m & 3));
                 m4 pc[4];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) pc[c] = m4{0.f, 0.f, 0.f, 0.f};
                 for (int e = 0; e < NE; e += 4) {
                     const float av = s_kt[(e + kr) * D + arow];
-                    const f4 bv = *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + 4 * m]);
+                    const f4 bv = *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + cq]);
 #pragma unroll
                     for (int c = 0; c < 4; ++c) pc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[c], pc[c], 0, 0, 0);
                 }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[4 * g + q][c] += pc[c][q];
+                    const int i = 4 * g + q;
+                    const f4 o = s[i] * s_scale[rbase + RSTEP * i] + f4{pc[0][q], pc[1][q], pc[2][q], pc[3][q]};
+                    __builtin_nontemporal_store(o, dst4 + (size_t)i * RSTEP * (D / 4));
                 }
             }
         } else {
+            f4 acc[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rbase + RSTEP * i];
             for (int e = 0; e < NE; e += 4) {
-                const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + 4 * cg]);
-                const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + 4 * cg]);
-                const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + 4 * cg]);
-                const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + 4 * cg]);
+                const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + cq]);
+                const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + cq]);
+                const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + cq]);
+                const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + cq]);
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    const int row = rs + RPP * i;
+                    const int row = rbase + RSTEP * i;
                     acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
                               s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
                 }
             }
-        }
-        f4 *dst4 = reinterpret_cast<f4 *>(p.base) + tile4;
 #pragma unroll
-        for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RPP * (D / 4));
+            for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RSTEP * (D / 4));
+        }
     }
 }
 
-// Tile shape of the chunk kernel: 64-column value tiles at D = 128 (32 KB,
-// 256 threads; 16 lanes per tile row, the layout of the matrix-core form),
-// whole heads below.  The K tokens' working set in LDS grows with the tile
-// width, so the chunk kernel keeps the narrower tile.
-template <int D>
+// Tile shape of the chunk kernel.  The matrix-core form (MM) takes whole heads
+// at D = 128 (64 KB, 256 threads of sixteen float4).  The vector form takes
+// 64-column value tiles at D = 128 (32 KB, 256 threads of eight float4): its
+// products reduce over the lanes of a tile row, and the K tokens' working set
+// in LDS grows with the tile width.  Whole heads below D = 128.
+template <int D, bool MM>
 struct ChunkShape {
-    static constexpr int TV = D == 128 ? 64 : D;
+    static constexpr int TV = D == 128 && !MM ? 64 : D;
     static constexpr int NT = D == 128 ? 256 : (D == 64 ? 128 : 64);
 };
 
+template <int OP, typename TIn, int D, int CMAX, bool MM>
+hipError_t launch_chunk_form(const ChunkParams &p, hipStream_t s) {
+    constexpr int TV = ChunkShape<D, MM>::TV, NT = ChunkShape<D, MM>::NT;
+    const unsigned blocks = (unsigned)p.N * (D / TV);
+    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, MM>), dim3(blocks), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+// matrix cores for the token products at d = 128 from three tokens on
+// (measured: fewer tokens, or the 16 KB tiles of d = 64, run faster on the
+// vector ALUs)
 template <int OP, typename TIn, int D, int CMAX>
 hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
-    constexpr int TV = ChunkShape<D>::TV, NT = ChunkShape<D>::NT;
-    const unsigned blocks = (unsigned)p.N * (D / TV);
-    // matrix cores for the token products at d = 128 from three tokens on
-    // (measured: fewer tokens, or the 16 KB tiles of d = 64, run faster on
-    // the vector ALUs)
     if constexpr (D == 128) {
-        if (p.K >= 3) {
-            hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, true>), dim3(blocks), dim3(NT), 0, s, p);
-            return hipGetLastError();
-        }
+        if (p.K >= 3) return launch_chunk_form<OP, TIn, D, CMAX, true>(p, s);
     }
-    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, false>), dim3(blocks), dim3(NT), 0, s, p);
-    return hipGetLastError();
+    return launch_chunk_form<OP, TIn, D, CMAX, false>(p, s);
 }
 
 template <int OP, typename TIn, int D>

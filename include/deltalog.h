@@ -145,8 +145,9 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *args, void *stream);
  * args[0..K-1] are the tokens in order, each as for dl_decode_step, and
  * args[t].out receives o_t.  The tokens share one read of the base: the log
  * grows by the chunk, and a chunk that fills the log folds it (a chunk that
- * would pass C is split there, one launch per part).  The result equals K
- * calls of dl_decode_step.  The RWKV6 bonus is a per-head parameter, so
+ * would pass C is split there, one launch per part; a part of one token is
+ * decoded by the single-token kernel, as dl_decode_step does).  The result
+ * equals K calls of dl_decode_step.  The RWKV6 bonus is a per-head parameter, so
  * every token must carry the same bonus pointer (DL_ERR_ARG otherwise).
  * On a per-slot handle, whose slots fill their
  * logs at different tokens, the tokens are decoded one launch each (the

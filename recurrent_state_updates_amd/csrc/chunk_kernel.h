@@ -57,12 +57,11 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
     return (global_ptr<E>)static_cast<const E *>(r);
 }
 
-// MM selects the matrix-core form of the token products (phase C); it pays
-// off from about three tokens on.  Its 16x16x4 k-steps are four rows of 64
-// columns, 16 lanes per (row, column range).  With TV = D = 128 it takes whole
-// heads: waves 2h and 2h + 1 hold column half h, rows 0-63 and 64-127, so a
-// head streams as one contiguous 64 KB block, its key-side work is done once,
-// and two waves' products add up per column.
+// MM selects the matrix-core form of the token products (phase C) and of the
+// fold, at D = 128.  A workgroup holds a whole head: waves 2h and 2h + 1 hold
+// column half h, rows 0-63 and 64-127, 16 lanes per (row, half), so that each
+// 16x16x4 k-step is four rows of one half and two waves' products add up per
+// column.  The vector form (D = 32, 64) holds whole heads as row passes.
 template <int OP, typename TIn, int D, int TV, int NT, int CMAX, bool MM>
 __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     using G = Geom<D, TV, NT>;
@@ -73,12 +72,12 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     constexpr int KM = KMAX_TOKENS;
     constexpr int CP = CMAX;  // entry slots: old entries plus the chunk's tokens (<= C <= CMAX)
     constexpr int KPASS = (CMAX + EPP - 1) / EPP;
-    constexpr bool WH = MM && TV == D;  // whole heads on the matrix cores
-    static_assert(!WH || (D == 128 && NT == 256), "whole-head matrix-core form: D = 128, 256 threads");
+    static_assert(!MM || (D == 128 && TV == D && NT == 256 && 2 * KM == 16),
+                  "matrix-core form: whole heads at D = 128, 256 threads, 16 product vectors");
     // s[i] holds tile row rbase + RSTEP * i; xrow[j] holds log entry ebase + ESTEP * j
-    constexpr int RSTEP = WH ? 4 : RPP;
-    constexpr int ESTEP = WH ? 8 : RPP;
-    constexpr int NWR = WH ? 2 : NW;  // row blocks whose products add up in each column
+    constexpr int RSTEP = MM ? 4 : RPP;
+    constexpr int ESTEP = MM ? 8 : RPP;
+    constexpr int NWR = MM ? 2 : NW;  // row blocks whose products add up in each column
     constexpr int XR = (CMAX + ESTEP - 1) / ESTEP;
     constexpr int GW = GDN ? 1 : D;  // log-decay values per entry
     using TX = typename std::conditional<DELTA, float, TIn>::type;
@@ -139,10 +138,10 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     const int last = L > 0 ? L - 1 : 0;
     // the thread's rows of the tile, its four columns (from cq, within the
     // tile) and its rows of the old log's value factors
-    const int rbase = WH ? 64 * (wave & 1) + (lane >> 4) : tid / LPR;
-    const int cq = WH ? 64 * (wave >> 1) + 4 * (lane & 15) : 4 * (tid % LPR);
-    const int ebase = WH ? 4 * (wave & 1) + (lane >> 4) : tid / LPR;
-    const int rblk = WH ? (wave & 1) : wave;
+    const int rbase = MM ? 64 * (wave & 1) + (lane >> 4) : tid / LPR;
+    const int cq = MM ? 64 * (wave >> 1) + 4 * (lane & 15) : 4 * (tid % LPR);
+    const int ebase = MM ? 4 * (wave & 1) + (lane >> 4) : tid / LPR;
+    const int rblk = MM ? (wave & 1) : wave;
     auto mv_at = [](int row) { return (row % RSTEP) * (D / RSTEP) + row / RSTEP; };
     const int col0 = tile * TV;
     const int c4 = 4 * (tid % KL);
@@ -383,7 +382,6 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     __syncthreads();
 
     // ---------------- Phase C: base products of every token from the register tile ----------------
-    static_assert(!MM || ((WH || LPR == 16) && 2 * KM == 16), "matrix-core form: 16 lanes per row, 16 vectors");
     if constexpr (MM) {
         // On the matrix cores: P[m][col] = sum_row A[m][row] S[row][col] over this
         // wave's rows, with the 16 vectors m = (side, token) = (m / 8, m % 8):
@@ -573,34 +571,25 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     }
 }
 
-// Tile shape of the chunk kernel.  The matrix-core form (MM) takes whole heads
-// at D = 128 (64 KB, 256 threads of sixteen float4).  The vector form takes
-// 64-column value tiles at D = 128 (32 KB, 256 threads of eight float4): its
-// products reduce over the lanes of a tile row, and the K tokens' working set
-// in LDS grows with the tile width.  Whole heads below D = 128.
-template <int D, bool MM>
+// Tile shape of the chunk kernel: one workgroup per head -- 64 KB over 256
+// threads of sixteen float4 at D = 128 (the matrix-core form), 16 KB over 128
+// threads at D = 64 and 4 KB over 64 threads at D = 32 (the vector form).
+template <int D>
 struct ChunkShape {
-    static constexpr int TV = D == 128 && !MM ? 64 : D;
+    static constexpr int TV = D;
     static constexpr int NT = D == 128 ? 256 : (D == 64 ? 128 : 64);
 };
 
-template <int OP, typename TIn, int D, int CMAX, bool MM>
-hipError_t launch_chunk_form(const ChunkParams &p, hipStream_t s) {
-    constexpr int TV = ChunkShape<D, MM>::TV, NT = ChunkShape<D, MM>::NT;
-    const unsigned blocks = (unsigned)p.N * (D / TV);
-    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, MM>), dim3(blocks), dim3(NT), 0, s, p);
-    return hipGetLastError();
-}
-
-// matrix cores for the token products at d = 128 from three tokens on
-// (measured: fewer tokens, or the 16 KB tiles of d = 64, run faster on the
-// vector ALUs)
+// The matrix cores form the token products at D = 128 (measured: whole heads
+// there run faster on them than on the vector ALUs from two tokens on; the
+// library sends a single token to the single-token kernel).  The 16 KB heads
+// of D = 64 and below stay on the vector ALUs.
 template <int OP, typename TIn, int D, int CMAX>
 hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
-    if constexpr (D == 128) {
-        if (p.K >= 3) return launch_chunk_form<OP, TIn, D, CMAX, true>(p, s);
-    }
-    return launch_chunk_form<OP, TIn, D, CMAX, false>(p, s);
+    constexpr int TV = ChunkShape<D>::TV, NT = ChunkShape<D>::NT;
+    const unsigned blocks = (unsigned)p.N;
+    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, D == 128>), dim3(blocks), dim3(NT), 0, s, p);
+    return hipGetLastError();
 }
 
 template <int OP, typename TIn, int D>

@@ -364,6 +364,12 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     const int bf16 = h->cfg.in_dtype == DL_BF16;
     for (int t0 = 0; t0 < K;) {
         const int k1 = std::min(K - t0, h->cfg.C - h->L);  // the part that fits the log
+        if (k1 == 1) {
+            // one token: the single-token kernel is faster than a chunk of one
+            if ((st = dl_decode_step(h, &args[t0], stream)) != DL_OK) return st;
+            t0 += 1;
+            continue;
+        }
         dlk::ChunkParams p = {};
         p.base = h->base;
         for (int t = 0; t < k1; ++t) {

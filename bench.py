@@ -79,7 +79,8 @@ def parse():
                     help="also time multi-token decode: K tokens per dl_decode_tokens call")
     ap.add_argument("--staggered", action="store_true",
                     help="also time per-slot logs with slot b starting at token b mod C, so that "
-                         "1/C of the slots fold at every step (continuous batching)")
+                         "1/C of the slots fold at every step (continuous batching); with --tokens K "
+                         "also K tokens per call on those slots")
     ap.add_argument("--split-ablation", action="store_true",
                     help="also time the fused and the split replay preparation, each launched call by "
                          "call and replayed as a captured merge-cycle graph")
@@ -311,6 +312,9 @@ def main():
 
     if args.staggered and C > 1:
         result["staggered"] = staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K)
+        if args.tokens > 1:
+            result["staggered"]["multi_token"] = staggered_multi_token_times(
+                dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K, args.tokens)
 
     if args.calibrate_copy:
         src = torch.empty(sh.heads * D * D, dtype=torch.float32, device=dev).fill_(1.0)
@@ -479,6 +483,74 @@ def staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K):
     return {"us_per_token": round(wall_us, 3), "events_us_per_token": round(ev_us, 3),
             "achieved_GBps": round(tok_bytes / (wall_us * 1e-6) / 1e9, 1),
             "note": "one launch per step; each slot appends, or folds when its token fills its log"}
+
+
+def staggered_multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K, ntok):
+    """Per-slot logs started as in staggered_times, decoded ntok tokens per
+    dl_decode_tokens call: each launch takes one segment of every slot's
+    tokens (up to its fold, then a fresh log)."""
+    import ctypes
+    import torch
+    base = d["S0"].clone()
+    st = dl.DeltaLogState(w.op, w.in_dtype, base, C, slots=True)
+    T = w.T
+    one = [st.step_args(d["q"][t], d["k"][t], d["v"][t], None if d["beta"] is None else d["beta"][t],
+                        d["decay"][t], d["bonus"], outs[t]) for t in range(T)]
+    lib = dl.load_library()
+    sptr = stream.cuda_stream
+    start, tok = {}, 0
+    for s_ in range(C):  # staggered starts, one token apart
+        for b in range(s_, Bsz, C):
+            st.activate(b)
+            start[b] = tok
+        assert lib.dl_decode_step(st.handle, ctypes.byref(one[tok % T]), sptr) == 0
+        tok += 1
+    ncalls = max(1, (K * C) // ntok)
+    warm = 3
+    calls = []
+    for _ in range(warm + ncalls):
+        calls.append((tok, (dl.StepArgs * ntok)(*[one[(tok + i) % T] for i in range(ntok)])))
+        tok += ntok
+    # modelled bytes of the timed calls: every slot's segments, as the library splits them
+    sh1 = traffic.Shape(sh.op, 1, sh.H, sh.d, sh.in_bytes)
+    nbytes = 0
+    for t0, _ in calls[warm:]:
+        nseg = 1
+        for b in range(Bsz):
+            L0 = (t0 - start[b]) % C
+            k = min(ntok, C - L0)
+            nbytes += chunk_bytes_slot(traffic, sh1, L0, k, L0 + k == C)
+            rem, segs = ntok - k, 1
+            while rem > 0:
+                k = min(rem, C)
+                nbytes += chunk_bytes_slot(traffic, sh1, 0, k, k == C)
+                rem -= k
+                segs += 1
+            nseg = max(nseg, segs)
+        nbytes += nseg * sh.shared()
+    for _, arr in calls[:warm]:
+        assert lib.dl_decode_tokens(st.handle, arr, ntok, sptr) == 0
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _, arr in calls[warm:]:
+        assert lib.dl_decode_tokens(st.handle, arr, ntok, sptr) == 0
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ntoks = ncalls * ntok
+    wall_us = (time.perf_counter() - t0) * 1e6 / ntoks
+    st.close()
+    return {"tokens_per_call": ntok, "us_per_token": round(wall_us, 3),
+            "events_us_per_token": round(e0.elapsed_time(e1) * 1e3 / ntoks, 3),
+            "model_MB_per_token": round(nbytes / ntoks / 1e6, 2),
+            "achieved_GBps": round(nbytes / ntoks / (wall_us * 1e-6) / 1e9, 1)}
+
+
+def chunk_bytes_slot(traffic, sh1, L, k, fold):
+    """One slot's share of a chunk launch (the per-launch bonus is counted apart)."""
+    return traffic.chunk_bytes(sh1, L, k, fold) - sh1.shared()
 
 
 def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs):

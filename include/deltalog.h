@@ -147,11 +147,15 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *args, void *stream);
  * grows by the chunk, and a chunk that fills the log folds it (a chunk that
  * would pass C is split there, one launch per part; a part of one token is
  * decoded by the single-token kernel, as dl_decode_step does).  The result
- * equals K calls of dl_decode_step.  The RWKV6 bonus is a per-head parameter, so
- * every token must carry the same bonus pointer (DL_ERR_ARG otherwise).
- * On a per-slot handle, whose slots fill their
- * logs at different tokens, the tokens are decoded one launch each (the
- * per-slot dl_decode_step), with the same result.  This is the multi-token
+ * equals K calls of dl_decode_step up to rounding.  The RWKV6 bonus is a
+ * per-head parameter, so every token must carry the same bonus pointer
+ * (DL_ERR_ARG otherwise).
+ * On a per-slot handle every slot's log fills at its own token: each launch
+ * takes one segment of every active slot's tokens (the first up to the
+ * slot's fold, then at most C tokens on an empty log), so a call makes as
+ * many launches as the slot with most segments needs (one or two when
+ * C >= K); inactive slots are untouched.  K == 1 is one
+ * dl_decode_step on either kind of handle.  This is the multi-token
  * neighbour of single-token decode (drafted tokens to verify, short
  * continuations); it follows from the same base-plus-log representation
  * (gist.science summary, "Meccanismo Core: Base + Log"). */

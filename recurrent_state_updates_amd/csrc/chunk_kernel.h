@@ -31,8 +31,8 @@ __device__ __forceinline__ void store_raw(bf16_bits *dst, float x) {
 }
 
 // Token pointers of the kernel arguments as opaque scalar values.  The lanes
-// of one wave belong to GPW consecutive key-side groups (tokens t0 .. t0 +
-// GPW - 1, t0 uniform), so each lane chooses among GPW pointers, each a
+// of one wave belong to GPW consecutive key-side groups (tokens tb + t0 .. tb
+// + t0 + GPW - 1, tb and t0 uniform), so each lane chooses among GPW pointers, each a
 // scalar load at a uniform index.  Left visible, the choice would be folded
 // back into an index into the argument array, read with a vector load that
 // the data load must wait for; the empty asm prevents that.  The result is
@@ -47,11 +47,11 @@ template <typename T>
 using global_ptr = const T __attribute__((address_space(1))) *;
 
 template <typename E, int GPW, typename T>
-__device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS], int t0, int K, int g) {
-    T r = opaque_scalar(arr[min(t0, K - 1)]);
+__device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS], int tb, int t0, int K, int g) {
+    T r = opaque_scalar(arr[tb + min(t0, K - 1)]);
 #pragma unroll
     for (int i = 1; i < GPW; ++i) {
-        const T c = opaque_scalar(arr[min(t0 + i, K - 1)]);
+        const T c = opaque_scalar(arr[tb + min(t0 + i, K - 1)]);
         r = g == i ? c : r;
     }
     return (global_ptr<E>)static_cast<const E *>(r);
@@ -131,9 +131,26 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     int n, tile;
     block_to_tile(blockIdx.x, p.N, NTILE, n, tile);
     const int C = p.C;
-    const int L = p.L;
-    const int K = p.K;
-    const bool fold = p.fold != 0;
+    // This workgroup's part of the call: tokens tb .. tb + K - 1 of the
+    // arguments, on a log of L entries, folding it when it fills.
+    int tb = 0, L = p.L, K = p.K;
+    bool fold = p.fold != 0;
+    if (p.slot_base != nullptr) {
+        // Per-slot logs: slot b held L0 entries before the call and fills at
+        // its own token.  Launch p.seg takes segment p.seg of the slot's
+        // tokens: the first runs up to its fold (or the call's end), each
+        // later one starts from an empty log.  The whole workgroup leaves
+        // together, before any barrier, when the slot is inactive or has no
+        // tokens left.
+        const int b = n / p.H;
+        if (!p.slot_active[b]) return;
+        const int L0 = (int)((p.step - (unsigned)p.slot_base[b]) % (unsigned)C);
+        tb = p.seg == 0 ? 0 : (C - L0) + (p.seg - 1) * C;
+        if (tb >= p.K) return;
+        L = p.seg == 0 ? L0 : 0;
+        K = min(p.K - tb, C - L);
+        fold = L + K == C;
+    }
     const int NE = L + K;               // entries after the chunk
     const int last = L > 0 ? L - 1 : 0;
     // the thread's rows of the tile, its four columns (from cq, within the
@@ -154,26 +171,26 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     constexpr int GPW = 64 / KL;  // key-side groups per wave
     const int t0 = __builtin_amdgcn_readfirstlane(tid >> 6) * GPW;
     const int g = lane / KL;      // ke = t0 + g
-    const Raw kraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.k, t0, K, g) + (size_t)n * D + c4);
-    const Raw qraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.q, t0, K, g) + (size_t)n * D + c4);
+    const Raw kraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.k, tb, t0, K, g) + (size_t)n * D + c4);
+    const Raw qraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.q, tb, t0, K, g) + (size_t)n * D + c4);
     f4 dec4 = {1.f, 1.f, 1.f, 1.f};
     float alpha = 1.f;
-    const global_ptr<float> dec_t = group_pick<float, GPW>(p.decay, t0, K, g);
+    const global_ptr<float> dec_t = group_pick<float, GPW>(p.decay, tb, t0, K, g);
     if (GDN)
         alpha = dec_t[n];
     else
         dec4 = *reinterpret_cast<global_ptr<f4>>(dec_t + (size_t)n * D + c4);
-    const float beta_t = DELTA ? group_pick<float, GPW>(p.beta, t0, K, g)[n] : 0.f;
+    const float beta_t = DELTA ? group_pick<float, GPW>(p.beta, tb, t0, K, g)[n] : 0.f;
     f4 bon4 = {0.f, 0.f, 0.f, 0.f};
     if (!DELTA) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
     // every token's value at this thread's column; slots past the chunk
     // re-read token 0 (a valid address) and are never used
     TIn vraw[KM];
     {
-        const void *v0 = opaque_scalar(p.v[0]);
+        const void *v0 = opaque_scalar(p.v[tb]);
 #pragma unroll
         for (int t = 0; t < KM; ++t) {
-            const void *vt = t == 0 ? v0 : opaque_scalar(p.v[t]);
+            const void *vt = t == 0 ? v0 : opaque_scalar(p.v[min(tb + t, KM - 1)]);
             vt = t < K ? vt : v0;
             vraw[t] = ((global_ptr<TIn>)static_cast<const TIn *>(vt))[(size_t)n * D + col0 + tid % TV];
         }
@@ -502,7 +519,7 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
                 o = zj + s_dot[t] * vj;
             }
             xs[t] = xnew;
-            p.out[t][(size_t)n * D + j] = o;
+            p.out[tb + t][(size_t)n * D + j] = o;
             if (fold) {
                 s_x[(L + t) * TV + jt] = xnew;
             } else {

@@ -353,26 +353,14 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     for (int t = 1; t < K; ++t)
         if (args[t].bonus != args[0].bonus)
             return fail(DL_ERR_ARG, "every token of a call must carry the same bonus");
-    if (h->slots) {
-        // every slot's log fills at its own token: one per-slot step per token
-        for (int t = 0; t < K; ++t)
-            if ((st = dl_decode_step(h, &args[t], stream)) != DL_OK) return st;
-        return DL_OK;
-    }
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const int cmax = cmax_of(&h->cfg);
     const int bf16 = h->cfg.in_dtype == DL_BF16;
-    for (int t0 = 0; t0 < K;) {
-        const int k1 = std::min(K - t0, h->cfg.C - h->L);  // the part that fits the log
-        if (k1 == 1) {
-            // one token: the single-token kernel is faster than a chunk of one
-            if ((st = dl_decode_step(h, &args[t0], stream)) != DL_OK) return st;
-            t0 += 1;
-            continue;
-        }
+    // tokens t0 .. t0 + k - 1 of the call as one chunk
+    auto chunk_of = [&](int t0, int k) {
         dlk::ChunkParams p = {};
         p.base = h->base;
-        for (int t = 0; t < k1; ++t) {
+        for (int t = 0; t < k; ++t) {
             const dl_step_args &a = args[t0 + t];
             p.q[t] = a.q;
             p.k[t] = a.k;
@@ -385,12 +373,13 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
         p.logX = h->logX;
         p.logK = h->logK;
         p.logG = h->logG;
-        p.L = h->L;
         p.C = h->cfg.C;
         p.H = h->cfg.H;
         p.N = (int)heads;
-        p.K = k1;
-        p.fold = h->L + k1 == h->cfg.C;
+        p.K = k;
+        return p;
+    };
+    auto launch_chunk = [&](const dlk::ChunkParams &p) -> dl_status {
         hipError_t e;
         switch (h->cfg.op) {
             case DL_GDN: e = dlk::launch_gdn_chunk(bf16, h->cfg.dk, cmax, p, s); break;
@@ -399,6 +388,43 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
         }
         if (e != hipSuccess)
             return fail(DL_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+        return DL_OK;
+    };
+    // one token: the single-token kernel is faster than a chunk of one
+    if (K == 1) return dl_decode_step(h, &args[0], stream);
+    if (h->slots) {
+        // Every slot's log fills at its own token.  Launch j takes segment j
+        // of each active slot's tokens: the first up to the slot's fold, then
+        // C at a time on an empty log.  The slots needing most segments set
+        // the number of launches.
+        const int C = h->cfg.C;
+        int nseg = 1;
+        for (int b = 0; b < h->cfg.B; ++b) {
+            const int room = C - slot_length(h, b);
+            if (h->h_active[b] && K > room) nseg = std::max(nseg, 1 + (K - room + C - 1) / C);
+        }
+        for (int seg = 0; seg < nseg; ++seg) {
+            dlk::ChunkParams p = chunk_of(0, K);
+            p.slot_base = h->slot_base;
+            p.slot_active = h->slot_active;
+            p.step = h->step;
+            p.seg = seg;
+            if ((st = launch_chunk(p)) != DL_OK) return st;
+        }
+        h->step += (unsigned)K;
+        return DL_OK;
+    }
+    for (int t0 = 0; t0 < K;) {
+        const int k1 = std::min(K - t0, h->cfg.C - h->L);  // the part that fits the log
+        if (k1 == 1) {
+            if ((st = dl_decode_step(h, &args[t0], stream)) != DL_OK) return st;
+            t0 += 1;
+            continue;
+        }
+        dlk::ChunkParams p = chunk_of(t0, k1);
+        p.L = h->L;
+        p.fold = h->L + k1 == h->cfg.C;
+        if ((st = launch_chunk(p)) != DL_OK) return st;
         h->L = p.fold ? 0 : h->L + k1;
         t0 += k1;
     }

@@ -59,7 +59,7 @@ hipError_t launch_gdn(int in_bf16, int D, int mode, int cmax, const StepParams &
 hipError_t launch_kda(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
 hipError_t launch_rwkv6(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
 
-// Several consecutive tokens of every head in one launch (lockstep log).
+// Several consecutive tokens of every head in one launch (lockstep or per-slot logs).
 constexpr int KMAX_TOKENS = 8;
 struct ChunkParams {
     float *base;                        // [N][D][D] fp32, rewritten in place when fold
@@ -79,6 +79,14 @@ struct ChunkParams {
     int N;
     int K;     // tokens in the chunk, 1 <= K <= KMAX_TOKENS
     int fold;  // 1: L + K == C, fold every entry into the base
+    // per-slot handles (slot_base != NULL): each slot's log length is
+    // (step - slot_base[b]) mod C and L, fold are ignored; the launch takes
+    // segment seg of every active slot's K tokens (segment 0 runs up to the
+    // slot's fold, each later one holds up to C tokens on an empty log)
+    const int *slot_base;
+    const unsigned char *slot_active;
+    unsigned step;
+    int seg;
 };
 
 hipError_t launch_gdn_chunk(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s);

@@ -339,8 +339,9 @@ def main():
 
 
 def multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K, ntok):
-    """K cycles of C tokens decoded ntok at a time with dl_decode_tokens."""
-    import ctypes
+    """About K cycles of C tokens, decoded ntok per dl_decode_tokens call (a
+    call that passes the log's end folds there and goes on in the same
+    launch)."""
     import torch
     base = d["S0"].clone()
     st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
@@ -349,42 +350,36 @@ def multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K, ntok)
                         d["decay"][t], d["bonus"], outs[t]) for t in range(T)]
     fn = dl.load_library().dl_decode_tokens
     sptr = stream.cuda_stream
-    # the call sequence of one cycle: chunk sizes as the library splits them at C
-    calls, left, L = [], C, 0
-    while left > 0:
-        k = min(ntok, C - L)
-        calls.append(k)
-        L = 0 if L + k == C else L + k
-        left -= k
     # every call's argument array is built before the timed region
-    ntot = 3 + K
+    nwarm = -(-3 * C // ntok)
+    ntimed = -(-K * C // ntok)
     schedule, tok = [], 0
-    for _ in range(ntot):
-        for k in calls:
-            schedule.append((k, (dl.StepArgs * k)(*[one[(tok + i) % T] for i in range(k)])))
-            tok += k
-    warm = 3 * len(calls)
+    for _ in range(nwarm + ntimed):
+        schedule.append((dl.StepArgs * ntok)(*[one[(tok + i) % T] for i in range(ntok)]))
+        tok += ntok
+    L0 = (nwarm * ntok) % C  # the log length when the timed calls start
 
     def run(lo, hi):
-        for k, arr in schedule[lo:hi]:
-            assert fn(st.handle, arr, k, sptr) == 0
+        for arr in schedule[lo:hi]:
+            assert fn(st.handle, arr, ntok, sptr) == 0
 
-    run(0, warm)
+    run(0, nwarm)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    run(warm, len(schedule))
+    run(nwarm, len(schedule))
     e1.record(stream)
     torch.cuda.synchronize()
-    wall_us = (time.perf_counter() - t0) * 1e6 / (K * C)
+    ntokens = ntimed * ntok
+    wall_us = (time.perf_counter() - t0) * 1e6 / ntokens
     st.close()
-    cyc = traffic.multi_token_cycle_bytes(sh, C, ntok)
+    nbytes = traffic.multi_token_bytes(sh, C, ntok, ntokens, L0)
     return {"tokens_per_call": ntok, "us_per_token": round(wall_us, 3),
-            "events_us_per_token": round(e0.elapsed_time(e1) * 1e3 / (K * C), 3),
-            "model_MB_per_token": round(cyc / C / 1e6, 2),
-            "achieved_GBps": round(cyc / C / (wall_us * 1e-6) / 1e9, 1)}
+            "events_us_per_token": round(e0.elapsed_time(e1) * 1e3 / ntokens, 3),
+            "model_MB_per_token": round(nbytes / ntokens / 1e6, 2),
+            "achieved_GBps": round(nbytes / ntokens / (wall_us * 1e-6) / 1e9, 1)}
 
 
 def split_ablation(dl, d, w, Bsz, C, dev, stream, outs, K):
@@ -487,8 +482,8 @@ def staggered_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K):
 
 def staggered_multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K, ntok):
     """Per-slot logs started as in staggered_times, decoded ntok tokens per
-    dl_decode_tokens call: each launch takes one segment of every slot's
-    tokens (up to its fold, then a fresh log)."""
+    dl_decode_tokens call: one launch, in which each slot folds when its log
+    fills and goes on from there."""
     import ctypes
     import torch
     base = d["S0"].clone()
@@ -511,23 +506,14 @@ def staggered_multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs
     for _ in range(warm + ncalls):
         calls.append((tok, (dl.StepArgs * ntok)(*[one[(tok + i) % T] for i in range(ntok)])))
         tok += ntok
-    # modelled bytes of the timed calls: every slot's segments, as the library splits them
+    # modelled bytes of the timed calls: one segmented launch per call, each
+    # slot from its own log length
     sh1 = traffic.Shape(sh.op, 1, sh.H, sh.d, sh.in_bytes)
     nbytes = 0
     for t0, _ in calls[warm:]:
-        nseg = 1
         for b in range(Bsz):
-            L0 = (t0 - start[b]) % C
-            k = min(ntok, C - L0)
-            nbytes += chunk_bytes_slot(traffic, sh1, L0, k, L0 + k == C)
-            rem, segs = ntok - k, 1
-            while rem > 0:
-                k = min(rem, C)
-                nbytes += chunk_bytes_slot(traffic, sh1, 0, k, k == C)
-                rem -= k
-                segs += 1
-            nseg = max(nseg, segs)
-        nbytes += nseg * sh.shared()
+            nbytes += traffic.call_bytes(sh1, (t0 - start[b]) % C, ntok, C) - sh1.shared()
+        nbytes += sh.shared()
     for _, arr in calls[:warm]:
         assert lib.dl_decode_tokens(st.handle, arr, ntok, sptr) == 0
     e0 = torch.cuda.Event(enable_timing=True)
@@ -546,11 +532,6 @@ def staggered_multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs
             "events_us_per_token": round(e0.elapsed_time(e1) * 1e3 / ntoks, 3),
             "model_MB_per_token": round(nbytes / ntoks / 1e6, 2),
             "achieved_GBps": round(nbytes / ntoks / (wall_us * 1e-6) / 1e9, 1)}
-
-
-def chunk_bytes_slot(traffic, sh1, L, k, fold):
-    """One slot's share of a chunk launch (the per-launch bonus is counted apart)."""
-    return traffic.chunk_bytes(sh1, L, k, fold) - sh1.shared()
 
 
 def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs):

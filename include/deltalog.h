@@ -143,22 +143,17 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *args, void *stream);
 
 /* Decode K consecutive tokens of every head (1 <= K <= DL_MAX_TOKENS):
  * args[0..K-1] are the tokens in order, each as for dl_decode_step, and
- * args[t].out receives o_t.  The tokens share one read of the base: the log
- * grows by the chunk, and a chunk that fills the log folds it (a chunk that
- * would pass C is split there, one launch per part; a part of one token is
- * decoded by the single-token kernel, as dl_decode_step does).  The result
+ * args[t].out receives o_t.  The tokens share one read of the base in one
+ * launch: the log grows by the call's tokens, and when it fills (at any
+ * token of the call) the kernel folds it into the base and goes on from the
+ * folded base with an empty log.  K == 1 is one dl_decode_step.  The result
  * equals K calls of dl_decode_step up to rounding.  The RWKV6 bonus is a
  * per-head parameter, so every token must carry the same bonus pointer
- * (DL_ERR_ARG otherwise).
- * On a per-slot handle every slot's log fills at its own token: each launch
- * takes one segment of every active slot's tokens (the first up to the
- * slot's fold, then at most C tokens on an empty log), so a call makes as
- * many launches as the slot with most segments needs (one or two when
- * C >= K); inactive slots are untouched.  K == 1 is one
- * dl_decode_step on either kind of handle.  This is the multi-token
- * neighbour of single-token decode (drafted tokens to verify, short
- * continuations); it follows from the same base-plus-log representation
- * (gist.science summary, "Meccanismo Core: Base + Log"). */
+ * (DL_ERR_ARG otherwise).  On a per-slot handle each slot folds at its own
+ * token, in the same single launch; inactive slots are untouched.  This is
+ * the multi-token neighbour of single-token decode (drafted tokens to
+ * verify, short continuations); it follows from the same base-plus-log
+ * representation (gist.science summary, "Meccanismo Core: Base + Log"). */
 dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *stream);
 
 /* Fold the current log into the base now (an early merge), L becomes 0.

@@ -62,8 +62,12 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
 // column half h, rows 0-63 and 64-127, 16 lanes per (row, half), so that each
 // 16x16x4 k-step is four rows of one half and two waves' products add up per
 // column.  The vector form (D = 32, 64) holds whole heads as row passes.
-template <int OP, typename TIn, int D, int TV, int NT, int CMAX, bool MM>
-__global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
+// SEG runs every segment of the call in one workgroup: when the log fills
+// before the call's last token, the fold updates the register tile in place
+// and the rest of the tokens start an empty log from it (per-slot handles,
+// and calls that pass C).  Without SEG the chunk fits the log.
+template <int OP, typename TIn, int D, int TV, int NT, int CMAX, bool MM, bool SEG>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SEG && MM && CMAX == 8 ? 3 : 1))) void chunk_kernel(const ChunkParams p) {
     using G = Geom<D, TV, NT>;
     constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
     constexpr int KL = G::KL, EPP = G::EPP;
@@ -131,27 +135,21 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     int n, tile;
     block_to_tile(blockIdx.x, p.N, NTILE, n, tile);
     const int C = p.C;
-    // This workgroup's part of the call: tokens tb .. tb + K - 1 of the
-    // arguments, on a log of L entries, folding it when it fills.
-    int tb = 0, L = p.L, K = p.K;
-    bool fold = p.fold != 0;
+    // The segment in hand: tokens tb .. tb + K - 1 of the arguments, on a log
+    // of L entries, folding it when it fills.
+    int tb = 0, L = p.L;
     if (p.slot_base != nullptr) {
-        // Per-slot logs: slot b held L0 entries before the call and fills at
-        // its own token.  Launch p.seg takes segment p.seg of the slot's
-        // tokens: the first runs up to its fold (or the call's end), each
-        // later one starts from an empty log.  The whole workgroup leaves
-        // together, before any barrier, when the slot is inactive or has no
-        // tokens left.
+        // Per-slot logs: slot b holds its own number of entries and fills at
+        // its own token.  The whole workgroup leaves together, before any
+        // barrier, when the slot is inactive.
         const int b = n / p.H;
         if (!p.slot_active[b]) return;
-        const int L0 = (int)((p.step - (unsigned)p.slot_base[b]) % (unsigned)C);
-        tb = p.seg == 0 ? 0 : (C - L0) + (p.seg - 1) * C;
-        if (tb >= p.K) return;
-        L = p.seg == 0 ? L0 : 0;
-        K = min(p.K - tb, C - L);
-        fold = L + K == C;
+        L = (int)((p.step - (unsigned)p.slot_base[b]) % (unsigned)C);
     }
-    const int NE = L + K;               // entries after the chunk
+    // with SEG the first segment runs up to the fold (or the call's end)
+    int K = SEG ? min(p.K, C - L) : p.K;
+    bool fold = SEG ? L + K == C : p.fold != 0;
+    int NE = L + K;                     // entries after the segment
     const int last = L > 0 ? L - 1 : 0;
     // the thread's rows of the tile, its four columns (from cq, within the
     // tile) and its rows of the old log's value factors
@@ -171,22 +169,22 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     constexpr int GPW = 64 / KL;  // key-side groups per wave
     const int t0 = __builtin_amdgcn_readfirstlane(tid >> 6) * GPW;
     const int g = lane / KL;      // ke = t0 + g
-    const Raw kraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.k, tb, t0, K, g) + (size_t)n * D + c4);
-    const Raw qraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.q, tb, t0, K, g) + (size_t)n * D + c4);
+    Raw kraw, qraw;
     f4 dec4 = {1.f, 1.f, 1.f, 1.f};
-    float alpha = 1.f;
-    const global_ptr<float> dec_t = group_pick<float, GPW>(p.decay, tb, t0, K, g);
-    if (GDN)
-        alpha = dec_t[n];
-    else
-        dec4 = *reinterpret_cast<global_ptr<f4>>(dec_t + (size_t)n * D + c4);
-    const float beta_t = DELTA ? group_pick<float, GPW>(p.beta, tb, t0, K, g)[n] : 0.f;
-    f4 bon4 = {0.f, 0.f, 0.f, 0.f};
-    if (!DELTA) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
-    // every token's value at this thread's column; slots past the chunk
-    // re-read token 0 (a valid address) and are never used
+    float alpha = 1.f, beta_t = 0.f;
     TIn vraw[KM];
-    {
+    // the segment's tokens: group ke's key side, and every token's value at
+    // this thread's column (slots past the segment re-read its first token,
+    // a valid address, and are never used)
+    auto load_tokens = [&]() {
+        kraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.k, tb, t0, K, g) + (size_t)n * D + c4);
+        qraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.q, tb, t0, K, g) + (size_t)n * D + c4);
+        const global_ptr<float> dec_t = group_pick<float, GPW>(p.decay, tb, t0, K, g);
+        if (GDN)
+            alpha = dec_t[n];
+        else
+            dec4 = *reinterpret_cast<global_ptr<f4>>(dec_t + (size_t)n * D + c4);
+        if (DELTA) beta_t = group_pick<float, GPW>(p.beta, tb, t0, K, g)[n];
         const void *v0 = opaque_scalar(p.v[tb]);
 #pragma unroll
         for (int t = 0; t < KM; ++t) {
@@ -194,7 +192,10 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
             vt = t < K ? vt : v0;
             vraw[t] = ((global_ptr<TIn>)static_cast<const TIn *>(vt))[(size_t)n * D + col0 + tid % TV];
         }
-    }
+    };
+    load_tokens();
+    f4 bon4 = {0.f, 0.f, 0.f, 0.f};
+    if (!DELTA) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
     float glast_s = 0.f;
     f4 glast4 = {0.f, 0.f, 0.f, 0.f};
     Raw klog[KPASS];
@@ -233,357 +234,389 @@ __global__ __launch_bounds__(NT) void chunk_kernel(const ChunkParams p) {
     // every load above is issued before anything consumes one (a consumer
     // scheduled among them would wait for all loads issued before it)
     __builtin_amdgcn_sched_barrier(0);
-    if (DELTA) s_beta[(c4 == 0 && ke < K) ? ke : KM] = beta_t;
     // matrix-core form: the values go to LDS here so that they hold no registers
-    // through phases B and C, which brings it to five workgroups per CU (every
-    // wave writes the same values; no branch, so that no load is sunk past the
-    // tile)
-    if constexpr (MM) {
+    // through phases B and C (every wave writes the same values; no branch, so
+    // that no load is sunk past the tile)
+    auto stage_tokens = [&]() {
+        if (DELTA) s_beta[(c4 == 0 && ke < K) ? ke : KM] = beta_t;
+        if constexpr (MM) {
 #pragma unroll
-        for (int t = 0; t < KM; ++t) s_x[(t < K ? L + t : CP) * TV + tid % TV] = to_f32(vraw[t]);
-    }
+            for (int t = 0; t < KM; ++t) s_x[(t < K ? L + t : CP) * TV + tid % TV] = to_f32(vraw[t]);
+        }
+    };
+    stage_tokens();
 
-    // ---------------- Phase B1: every token's inputs into LDS (group ke = token) ----------------
-    const f4 kt_in = In4<TIn>::unpack(kraw);
-    const f4 qt_in = In4<TIn>::unpack(qraw);
-    if (ke < K) {
-        *reinterpret_cast<f4 *>(&s_k[ke][c4]) = kt_in;
-        *reinterpret_cast<f4 *>(&s_q[ke][c4]) = qt_in;
-        if (GDN) {
-            if (c4 == 0) s_lg[ke][0] = log2f(alpha);
-        } else {
-            *reinterpret_cast<f4 *>(&s_lg[ke][c4]) = log2v(dec4);
+    // One segment of the call.  The first may replay the old log; a later one
+    // starts from an empty log, so its code (FIRST false) holds none of the
+    // old entries' registers.
+    auto run_segment = [&](auto first_tag) {
+        constexpr bool FIRST = decltype(first_tag)::value;
+
+        // ---------------- Phase B1: every token's inputs into LDS (group ke = token) ----------------
+        const f4 kt_in = In4<TIn>::unpack(kraw);
+        const f4 qt_in = In4<TIn>::unpack(qraw);
+        if (ke < K) {
+            *reinterpret_cast<f4 *>(&s_k[ke][c4]) = kt_in;
+            *reinterpret_cast<f4 *>(&s_q[ke][c4]) = qt_in;
+            if (GDN) {
+                if (c4 == 0) s_lg[ke][0] = log2f(alpha);
+            } else {
+                *reinterpret_cast<f4 *>(&s_lg[ke][c4]) = log2v(dec4);
+            }
         }
-    }
-    if (ke == 0) {  // g_{-1} = g_L, newest old entry's cumulative log-decay
-        if (GDN) {
-            if (c4 == 0) s_g[0][0] = L > 0 ? glast_s : 0.f;
-        } else {
-            *reinterpret_cast<f4 *>(&s_g[0][c4]) = L > 0 ? glast4 : f4{0.f, 0.f, 0.f, 0.f};
+        if (ke == 0) {  // g_{-1} = g_L, newest old entry's cumulative log-decay
+            if (GDN) {
+                if (c4 == 0) s_g[0][0] = FIRST && L > 0 ? glast_s : 0.f;
+            } else {
+                *reinterpret_cast<f4 *>(&s_g[0][c4]) = FIRST && L > 0 ? glast4 : f4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-    }
-    __syncthreads();
-    // prefix sums of the log-decays: g_t for every token (group 0, four channels per thread)
-    if (ke == 0) {
-        if (GDN) {
-            if (c4 == 0) {
-                float g = s_g[0][0];
+        __syncthreads();
+        // prefix sums of the log-decays: g_t for every token (group 0, four channels per thread)
+        if (ke == 0) {
+            if (GDN) {
+                if (c4 == 0) {
+                    float g = s_g[0][0];
+                    for (int t = 0; t < K; ++t) {
+                        g += s_lg[t][0];
+                        s_g[t + 1][0] = g;
+                    }
+                }
+            } else {
+                f4 g = *reinterpret_cast<const f4 *>(&s_g[0][c4]);
                 for (int t = 0; t < K; ++t) {
-                    g += s_lg[t][0];
-                    s_g[t + 1][0] = g;
+                    g += *reinterpret_cast<const f4 *>(&s_lg[t][c4]);
+                    *reinterpret_cast<f4 *>(&s_g[t + 1][c4]) = g;
                 }
             }
-        } else {
-            f4 g = *reinterpret_cast<const f4 *>(&s_g[0][c4]);
-            for (int t = 0; t < K; ++t) {
-                g += *reinterpret_cast<const f4 *>(&s_lg[t][c4]);
-                *reinterpret_cast<f4 *>(&s_g[t + 1][c4]) = g;
-            }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    auto g_at = [&](int idx) -> f4 {  // g_{idx-1} for the thread's four channels
-        if (GDN) {
-            const float g = s_g[idx][0];
-            return f4{g, g, g, g};
-        }
-        return *reinterpret_cast<const f4 *>(&s_g[idx][c4]);
-    };
-
-    // ---------------- Phase B2: per token: scaled key / query, dot, log append ----------------
-    {
-        // every group reduces its (valid, clamped) token's dot so that the lane
-        // exchanges run with the whole wave active
-        float part;
-        if (DELTA)
-            part = dot4(kt_in, qt_in);
-        else
-            part = dot4(qt_in * bon4, kt_in);
-        part = group_sum_valu<KL>(part);
-        if (ke < K && c4 == 0) s_dot[ke] = part;
-    }
-    if (ke < K) {
-        const int t = ke;
-        const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
-        const f4 sc = exp2v(rho);
-        const f4 m0 = sc * kt_in, m1 = sc * qt_in;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int at = mv_at(c4 + c);
-            if (DELTA) s_mv0[t][at] = m0[c];
-            s_mv1[t][at] = m1[c];
-        }
-        if (!fold && tile == 0) {  // entry L + t of the log: the key copy and its log-decay
-            const size_t e = (size_t)n * C + L + t;
-            *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * D + c4) = kraw;
+        auto g_at = [&](int idx) -> f4 {  // g_{idx-1} for the thread's four channels
             if (GDN) {
-                if (c4 == 0) p.logG[e] = g_at(t + 1).x;
-            } else {
-                *reinterpret_cast<f4 *>(p.logG + e * D + c4) = g_at(t + 1);
+                const float g = s_g[idx][0];
+                return f4{g, g, g, g};
             }
-        }
-    }
-    if (fold && ke == 0) *reinterpret_cast<f4 *>(&s_scale[c4]) = exp2v(g_at(K));
+            return *reinterpret_cast<const f4 *>(&s_g[idx][c4]);
+        };
 
-    // ---------------- Phase B3: coefficients of every (token, entry) pair ----------------
-    const f4 gend = g_at(K);  // g_{K-1}: the fold's decay point
-#pragma unroll
-    for (int ps = 0; ps < KPASS; ++ps) {
-        const int e = ps * EPP + ke;
-        const bool is_old = e < L;
-        const bool is_new = e >= L && e < NE;
-        f4 ke4, ge4;
-        if (is_old) {
-            ke4 = In4<TIn>::unpack(klog[ps]);
-            ge4 = GDN ? f4{glog_s[ps], glog_s[ps], glog_s[ps], glog_s[ps]} : glog4[ps];
-        } else if (is_new) {
-            ke4 = *reinterpret_cast<const f4 *>(&s_k[e - L][c4]);
-            ge4 = g_at(e - L + 1);
-        } else {
-            ke4 = f4{0.f, 0.f, 0.f, 0.f};
-            ge4 = f4{0.f, 0.f, 0.f, 0.f};
+        // ---------------- Phase B2: per token: scaled key / query, dot, log append ----------------
+        {
+            // every group reduces its (valid, clamped) token's dot so that the lane
+            // exchanges run with the whole wave active
+            float part;
+            if (DELTA)
+                part = dot4(kt_in, qt_in);
+            else
+                part = dot4(qt_in * bon4, kt_in);
+            part = group_sum_valu<KL>(part);
+            if (ke < K && c4 == 0) s_dot[ke] = part;
         }
-        // every token's partial dots first, then one batch of lane reductions
-        float pk[KM], pq[KM];
+        if (ke < K) {
+            const int t = ke;
+            const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
+            const f4 sc = exp2v(rho);
+            const f4 m0 = sc * kt_in, m1 = sc * qt_in;
 #pragma unroll
-        for (int t = 0; t < KM; ++t) {
-            pk[t] = 0.f;
-            pq[t] = 0.f;
-            if (t < K && (is_old || (is_new && e - L < t))) {
-                const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
-                const f4 kt = ke4 * exp2v(rho - ge4);
-                if (DELTA) pk[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_k[t][c4]));
-                pq[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_q[t][c4]));
+            for (int c = 0; c < 4; ++c) {
+                const int at = mv_at(c4 + c);
+                if (DELTA) s_mv0[t][at] = m0[c];
+                s_mv1[t][at] = m1[c];
+            }
+            if (!fold && tile == 0) {  // entry L + t of the log: the key copy and its log-decay
+                const size_t e = (size_t)n * C + L + t;
+                *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * D + c4) = kraw;
+                if (GDN) {
+                    if (c4 == 0) p.logG[e] = g_at(t + 1).x;
+                } else {
+                    *reinterpret_cast<f4 *>(p.logG + e * D + c4) = g_at(t + 1);
+                }
             }
         }
-        // in batches of four tokens, so that the independent exchanges of a
-        // batch interleave; the second batch only when the chunk reaches it
-        // (RWKV6 needs no key-side coefficients)
+        if (fold && ke == 0) *reinterpret_cast<f4 *>(&s_scale[c4]) = exp2v(g_at(K));
+
+        // ---------------- Phase B3: coefficients of every (token, entry) pair ----------------
+        const f4 gend = g_at(K);  // g_{K-1}: the fold's decay point
 #pragma unroll
-        for (int h = 0; h < KM; h += 4) {
-            if (h > 0 && K <= h) break;
-#pragma unroll
-            for (int t = h; t < h + 4; ++t) {
-                if (DELTA) pk[t] = group_sum_valu<KL>(pk[t]);
-                pq[t] = group_sum_valu<KL>(pq[t]);
+        for (int ps = 0; ps < KPASS; ++ps) {
+            const int e = ps * EPP + ke;
+            const bool is_old = FIRST && e < L;
+            const bool is_new = e >= L && e < NE;
+            f4 ke4, ge4;
+            if (is_old) {
+                ke4 = In4<TIn>::unpack(klog[ps]);
+                ge4 = GDN ? f4{glog_s[ps], glog_s[ps], glog_s[ps], glog_s[ps]} : glog4[ps];
+            } else if (is_new) {
+                ke4 = *reinterpret_cast<const f4 *>(&s_k[e - L][c4]);
+                ge4 = g_at(e - L + 1);
+            } else {
+                ke4 = f4{0.f, 0.f, 0.f, 0.f};
+                ge4 = f4{0.f, 0.f, 0.f, 0.f};
             }
-        }
-        if (c4 == 0 && e < NE) {
+            // every token's partial dots first, then one batch of lane reductions
+            float pk[KM], pq[KM];
 #pragma unroll
             for (int t = 0; t < KM; ++t) {
-                if (t < K) {
-                    if (DELTA) s_coef[0][t][e] = pk[t];
-                    s_coef[1][t][e] = pq[t];
+                pk[t] = 0.f;
+                pq[t] = 0.f;
+                if (t < K && (is_old || (is_new && e - L < t))) {
+                    const f4 rho = DELTA ? g_at(t + 1) : g_at(t);
+                    const f4 kt = ke4 * exp2v(rho - ge4);
+                    if (DELTA) pk[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_k[t][c4]));
+                    pq[t] = dot4(kt, *reinterpret_cast<const f4 *>(&s_q[t][c4]));
                 }
             }
-        }
-        if (fold && (is_old || is_new))
-            *reinterpret_cast<f4 *>(&s_kt[e * D + c4]) = ke4 * exp2v(gend - ge4);
-    }
-    if (fold) {
-        // old value factors of the tile for the fold; zero the slots up to a multiple of four
+            // in batches of four tokens, so that the independent exchanges of a
+            // batch interleave; the second batch only when the chunk reaches it
+            // (RWKV6 needs no key-side coefficients)
 #pragma unroll
-        for (int j = 0; j < XR; ++j) {
-            const int i = ebase + ESTEP * j;
-            if (i < L) *reinterpret_cast<f4 *>(&s_x[i * TV + cq]) = In4<TX>::unpack(xrow[j]);
-        }
-        const int pad = ((NE + 3) & ~3) - NE;
-        for (int idx = tid; idx < pad * D; idx += NT) {
-            const int i = NE + idx / D;
-            const int c = idx % D;
-            s_kt[i * D + c] = 0.f;
-            if (c < TV) s_x[i * TV + c] = 0.f;
-        }
-    }
-    __syncthreads();
-
-    // ---------------- Phase C: base products of every token from the register tile ----------------
-    if constexpr (MM) {
-        // On the matrix cores: P[m][col] = sum_row A[m][row] S[row][col] over this
-        // wave's rows, with the 16 vectors m = (side, token) = (m / 8, m % 8):
-        // side 0 the scaled keys, side 1 the scaled queries (receptances).  The
-        // register tile already has the 16x16x4 operand layout: in k-step i,
-        // lane l holds row rbase + RSTEP i (rbase = its wave's first row + l/16)
-        // and columns cq + c (cq = its wave's first column + 4 (l % 16)), so
-        // component c of s[i] is the B operand of the c-th product, and lane l
-        // supplies A[l % 16][that row].  The old log joins as XR more k-steps
-        // with the replay coefficients as A and the logged value rows as B.
-        typedef float m4 __attribute__((ext_vector_type(4)));
-        const int m = lane & 15;
-        const int kr = lane >> 4;
-        const int side = m >> 3, tm = m & 7;
-        // RWKV6 has only the query side: its key-side vectors are zero
-        const bool live = tm < K && (DELTA || side == 1);
-        const float *mv = (side || !DELTA) ? &s_mv1[tm][0] : &s_mv0[tm][0];
-        float a[R];
+            for (int h = 0; h < KM; h += 4) {
+                if (h > 0 && K <= h) break;
 #pragma unroll
-        for (int i4 = 0; i4 < R / 4; ++i4) {
-            const f4 v = *reinterpret_cast<const f4 *>(&mv[mv_at(rbase) + 4 * i4]);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) a[4 * i4 + c] = live ? v[c] : 0.f;
-        }
-        // the products below are written over the scaled vectors
-        __syncthreads();
-        m4 acc[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[c] = m4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], s[i][c], acc[c], 0, 0, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < XR; ++j) {
-            // entries at or past L were loaded from a clamped index and may be
-            // anything (an unused slot holds whatever the workspace held): zero
-            // both operands, since 0 * NaN would poison the sum
-            const int e = ebase + ESTEP * j;
-            const float co = (live && e < L) ? s_coef[side][tm][e] : 0.f;
-            const f4 xv = e < L ? In4<TX>::unpack(xrow[j]) : f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(co, xv[c], acc[c], 0, 0, 0);
-        }
-        // lane l holds P[4 (l / 16) + q][cq + c] in acc[c][q]
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int mo = 4 * kr + q;
-            if (DELTA || (mo >> 3) == 1)
-                *reinterpret_cast<f4 *>(&s_red[mo & 7][rblk][DELTA ? (mo >> 3) : 0][cq]) =
-                    f4{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
-        }
-    } else {
-#pragma unroll
-        for (int t = 0; t < KM; ++t) {
-            if (t >= K) break;
-            f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int i4 = 0; i4 < R / 4; ++i4) {
-                const f4 a = DELTA ? *reinterpret_cast<const f4 *>(&s_mv0[t][mv_at(rbase) + 4 * i4]) : f4{0.f, 0.f, 0.f, 0.f};
-                const f4 b = *reinterpret_cast<const f4 *>(&s_mv1[t][mv_at(rbase) + 4 * i4]);
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    if (DELTA) y += s[4 * i4 + c] * a[c];
-                    z += s[4 * i4 + c] * b[c];
+                for (int t = h; t < h + 4; ++t) {
+                    if (DELTA) pk[t] = group_sum_valu<KL>(pk[t]);
+                    pq[t] = group_sum_valu<KL>(pq[t]);
                 }
             }
+            if (c4 == 0 && e < NE) {
+#pragma unroll
+                for (int t = 0; t < KM; ++t) {
+                    if (t < K) {
+                        if (DELTA) s_coef[0][t][e] = pk[t];
+                        s_coef[1][t][e] = pq[t];
+                    }
+                }
+            }
+            if (fold && (is_old || is_new))
+                *reinterpret_cast<f4 *>(&s_kt[e * D + c4]) = ke4 * exp2v(gend - ge4);
+        }
+        if (fold) {
+            // old value factors of the tile for the fold; zero the slots up to a multiple of four
 #pragma unroll
             for (int j = 0; j < XR; ++j) {
                 const int i = ebase + ESTEP * j;
-                if (i < L) {
-                    const f4 x = In4<TX>::unpack(xrow[j]);
-                    if (DELTA) y += s_coef[0][t][i] * x;
-                    z += s_coef[1][t][i] * x;
-                }
+                if (FIRST && i < L) *reinterpret_cast<f4 *>(&s_x[i * TV + cq]) = In4<TX>::unpack(xrow[j]);
             }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (DELTA) y[c] = column_sum_valu<LPR>(y[c]);
-                z[c] = column_sum_valu<LPR>(z[c]);
-            }
-            if (lane < LPR) {
-                if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][rblk][0][cq]) = y;
-                *reinterpret_cast<f4 *>(&s_red[t][rblk][ZS][cq]) = z;
+            const int pad = ((NE + 3) & ~3) - NE;
+            for (int idx = tid; idx < pad * D; idx += NT) {
+                const int i = NE + idx / D;
+                const int c = idx % D;
+                s_kt[i * D + c] = 0.f;
+                if (c < TV) s_x[i * TV + c] = 0.f;
             }
         }
-    }
-    __syncthreads();
-
-    // ---------------- Phase D: per column, the chunk's tokens in order ----------------
-    if (tid < TV) {
-        const int jt = tid;
-        const int j = col0 + jt;
-        float xs[KM];  // value factors of the chunk's tokens in this column
-#pragma unroll
-        for (int t = 0; t < KM; ++t) {
-            if (t >= K) break;
-            float yj = 0.f, zj = 0.f;
-#pragma unroll
-            for (int w = 0; w < NWR; ++w) {
-                if (DELTA) yj += s_red[t][w][0][jt];
-                zj += s_red[t][w][ZS][jt];
-            }
-#pragma unroll
-            for (int m = 0; m < KM; ++m) {
-                if (m >= t) break;
-                if (DELTA) yj += s_coef[0][t][L + m] * xs[m];
-                zj += s_coef[1][t][L + m] * xs[m];
-            }
-            const float vj = MM ? s_x[(L + t) * TV + jt] : to_f32(vraw[t]);
-            float xnew, o;
-            if (DELTA) {
-                xnew = s_beta[t] * (vj - yj);
-                o = zj + s_dot[t] * xnew;
-            } else {
-                xnew = vj;
-                o = zj + s_dot[t] * vj;
-            }
-            xs[t] = xnew;
-            p.out[tb + t][(size_t)n * D + j] = o;
-            if (fold) {
-                s_x[(L + t) * TV + jt] = xnew;
-            } else {
-                const size_t e = (size_t)n * C + L + t;
-                if (DELTA)
-                    static_cast<float *>(p.logX)[e * D + j] = xnew;
-                else
-                    store_raw(static_cast<TIn *>(p.logX) + e * D + j, vj);
-            }
-        }
-    }
-
-    // ---------------- Phase E: fold every entry into the base when the chunk fills the log ----------------
-    if (fold) {
         __syncthreads();
-        f4 *dst4 = reinterpret_cast<f4 *>(p.base) + tile4;
+
+        // ---------------- Phase C: base products of every token from the register tile ----------------
         if constexpr (MM) {
-            // The rank-NE update on the matrix cores.  For row group g and
-            // column offset c: P[M][n] = sum_e kt[e][row(M)] x[e][4 n + c] (columns
-            // from the wave's first) with row(M) = the wave's first row + M / 4 +
-            // RSTEP (4 g + M % 4), so that lane l ends with P[4 (l / 16) + q][l % 16]
-            // = the update of its own s[4 g + q][c].  Each group's rows are stored
-            // as soon as they are done, so that one group's products are live at
-            // a time.
-            // The entry slots past NE are zero up to a multiple of four.
+            // On the matrix cores: P[m][col] = sum_row A[m][row] S[row][col] over this
+            // wave's rows, with the 16 vectors m = (side, token) = (m / 8, m % 8):
+            // side 0 the scaled keys, side 1 the scaled queries (receptances).  The
+            // register tile already has the 16x16x4 operand layout: in k-step i,
+            // lane l holds row rbase + RSTEP i (rbase = its wave's first row + l/16)
+            // and columns cq + c (cq = its wave's first column + 4 (l % 16)), so
+            // component c of s[i] is the B operand of the c-th product, and lane l
+            // supplies A[l % 16][that row].  The old log joins as XR more k-steps
+            // with the replay coefficients as A and the logged value rows as B.
             typedef float m4 __attribute__((ext_vector_type(4)));
-            const int m = lane & 15, kr = lane >> 4;
+            const int m = lane & 15;
+            const int kr = lane >> 4;
+            const int side = m >> 3, tm = m & 7;
+            // RWKV6 has only the query side: its key-side vectors are zero
+            const bool live = tm < K && (DELTA || side == 1);
+            const float *mv = (side || !DELTA) ? &s_mv1[tm][0] : &s_mv0[tm][0];
+            float a[R];
 #pragma unroll
-            for (int g = 0; g < R / 4; ++g) {
-                const int arow = rbase - kr + (m >> 2) + RSTEP * (4 * g + (m & 3));
-                m4 pc[4];
+            for (int i4 = 0; i4 < R / 4; ++i4) {
+                const f4 v = *reinterpret_cast<const f4 *>(&mv[mv_at(rbase) + 4 * i4]);
 #pragma unroll
-                for (int c = 0; c < 4; ++c) pc[c] = m4{0.f, 0.f, 0.f, 0.f};
-                for (int e = 0; e < NE; e += 4) {
-                    const float av = s_kt[(e + kr) * D + arow];
-                    const f4 bv = *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + cq]);
+                for (int c = 0; c < 4; ++c) a[4 * i4 + c] = live ? v[c] : 0.f;
+            }
+            // the products below are written over the scaled vectors
+            __syncthreads();
+            m4 acc[4];
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) pc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[c], pc[c], 0, 0, 0);
-                }
+            for (int c = 0; c < 4; ++c) acc[c] = m4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int i = 4 * g + q;
-                    const f4 o = s[i] * s_scale[rbase + RSTEP * i] + f4{pc[0][q], pc[1][q], pc[2][q], pc[3][q]};
-                    __builtin_nontemporal_store(o, dst4 + (size_t)i * RSTEP * (D / 4));
-                }
+            for (int i = 0; i < R; ++i) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], s[i][c], acc[c], 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < XR; ++j) {
+                // entries at or past L were loaded from a clamped index and may be
+                // anything (an unused slot holds whatever the workspace held): zero
+                // both operands, since 0 * NaN would poison the sum
+                const int e = ebase + ESTEP * j;
+                const float co = (FIRST && live && e < L) ? s_coef[side][tm][e] : 0.f;
+                const f4 xv = FIRST && e < L ? In4<TX>::unpack(xrow[j]) : f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(co, xv[c], acc[c], 0, 0, 0);
+            }
+            // lane l holds P[4 (l / 16) + q][cq + c] in acc[c][q]
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int mo = 4 * kr + q;
+                if (DELTA || (mo >> 3) == 1)
+                    *reinterpret_cast<f4 *>(&s_red[mo & 7][rblk][DELTA ? (mo >> 3) : 0][cq]) =
+                        f4{acc[0][q], acc[1][q], acc[2][q], acc[3][q]};
             }
         } else {
-            f4 acc[R];
 #pragma unroll
-            for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rbase + RSTEP * i];
-            for (int e = 0; e < NE; e += 4) {
-                const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + cq]);
-                const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + cq]);
-                const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + cq]);
-                const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + cq]);
+            for (int t = 0; t < KM; ++t) {
+                if (t >= K) break;
+                f4 y = {0.f, 0.f, 0.f, 0.f}, z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const int row = rbase + RSTEP * i;
-                    acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
-                              s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
+                for (int i4 = 0; i4 < R / 4; ++i4) {
+                    const f4 a = DELTA ? *reinterpret_cast<const f4 *>(&s_mv0[t][mv_at(rbase) + 4 * i4]) : f4{0.f, 0.f, 0.f, 0.f};
+                    const f4 b = *reinterpret_cast<const f4 *>(&s_mv1[t][mv_at(rbase) + 4 * i4]);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        if (DELTA) y += s[4 * i4 + c] * a[c];
+                        z += s[4 * i4 + c] * b[c];
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < XR; ++j) {
+                    const int i = ebase + ESTEP * j;
+                    if (FIRST && i < L) {
+                        const f4 x = In4<TX>::unpack(xrow[j]);
+                        if (DELTA) y += s_coef[0][t][i] * x;
+                        z += s_coef[1][t][i] * x;
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if (DELTA) y[c] = column_sum_valu<LPR>(y[c]);
+                    z[c] = column_sum_valu<LPR>(z[c]);
+                }
+                if (lane < LPR) {
+                    if (DELTA) *reinterpret_cast<f4 *>(&s_red[t][rblk][0][cq]) = y;
+                    *reinterpret_cast<f4 *>(&s_red[t][rblk][ZS][cq]) = z;
                 }
             }
+        }
+        __syncthreads();
+
+        // ---------------- Phase D: per column, the chunk's tokens in order ----------------
+        if (tid < TV) {
+            const int jt = tid;
+            const int j = col0 + jt;
+            float xs[KM];  // value factors of the chunk's tokens in this column
 #pragma unroll
-            for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RSTEP * (D / 4));
+            for (int t = 0; t < KM; ++t) {
+                if (t >= K) break;
+                float yj = 0.f, zj = 0.f;
+#pragma unroll
+                for (int w = 0; w < NWR; ++w) {
+                    if (DELTA) yj += s_red[t][w][0][jt];
+                    zj += s_red[t][w][ZS][jt];
+                }
+#pragma unroll
+                for (int m = 0; m < KM; ++m) {
+                    if (m >= t) break;
+                    if (DELTA) yj += s_coef[0][t][L + m] * xs[m];
+                    zj += s_coef[1][t][L + m] * xs[m];
+                }
+                const float vj = MM ? s_x[(L + t) * TV + jt] : to_f32(vraw[t]);
+                float xnew, o;
+                if (DELTA) {
+                    xnew = s_beta[t] * (vj - yj);
+                    o = zj + s_dot[t] * xnew;
+                } else {
+                    xnew = vj;
+                    o = zj + s_dot[t] * vj;
+                }
+                xs[t] = xnew;
+                p.out[tb + t][(size_t)n * D + j] = o;
+                if (fold) {
+                    s_x[(L + t) * TV + jt] = xnew;
+                } else {
+                    const size_t e = (size_t)n * C + L + t;
+                    if (DELTA)
+                        static_cast<float *>(p.logX)[e * D + j] = xnew;
+                    else
+                        store_raw(static_cast<TIn *>(p.logX) + e * D + j, vj);
+                }
+            }
+        }
+
+        // ---------------- Phase E: fold every entry into the base when the chunk fills the log ----------------
+        if (fold) {
+            __syncthreads();
+            f4 *dst4 = reinterpret_cast<f4 *>(p.base) + tile4;
+            if constexpr (MM) {
+                // The rank-NE update on the matrix cores.  For row group g and
+                // column offset c: P[M][n] = sum_e kt[e][row(M)] x[e][4 n + c] (columns
+                // from the wave's first) with row(M) = the wave's first row + M / 4 +
+                // RSTEP (4 g + M % 4), so that lane l ends with P[4 (l / 16) + q][l % 16]
+                // = the update of its own s[4 g + q][c].  Each group's rows are stored
+                // as soon as they are done, so that one group's products are live at
+                // a time.
+                // The entry slots past NE are zero up to a multiple of four.
+                typedef float m4 __attribute__((ext_vector_type(4)));
+                const int m = lane & 15, kr = lane >> 4;
+#pragma unroll
+                for (int g = 0; g < R / 4; ++g) {
+                    const int arow = rbase - kr + (m >> 2) + RSTEP * (4 * g + (m & 3));
+                    m4 pc[4];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) pc[c] = m4{0.f, 0.f, 0.f, 0.f};
+                    for (int e = 0; e < NE; e += 4) {
+                        const float av = s_kt[(e + kr) * D + arow];
+                        const f4 bv = *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + cq]);
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) pc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[c], pc[c], 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int i = 4 * g + q;
+                        const f4 o = s[i] * s_scale[rbase + RSTEP * i] + f4{pc[0][q], pc[1][q], pc[2][q], pc[3][q]};
+                        __builtin_nontemporal_store(o, dst4 + (size_t)i * RSTEP * (D / 4));
+                        if constexpr (SEG) s[i] = o;
+                    }
+                }
+            } else {
+                f4 acc[R];
+#pragma unroll
+                for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rbase + RSTEP * i];
+                for (int e = 0; e < NE; e += 4) {
+                    const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + cq]);
+                    const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + cq]);
+                    const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + cq]);
+                    const f4 x3 = *reinterpret_cast<const f4 *>(&s_x[(e + 3) * TV + cq]);
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        const int row = rbase + RSTEP * i;
+                        acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
+                                  s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RSTEP * (D / 4));
+                if constexpr (SEG) {
+#pragma unroll
+                    for (int i = 0; i < R; ++i) s[i] = acc[i];
+                }
+            }
+        }
+
+    };
+    run_segment(std::true_type{});
+    if constexpr (SEG) {
+        // the next segments: the rest of the call's tokens, each on an empty
+        // log from the base the fold left in registers
+        for (;;) {
+            tb += K;
+            if (tb >= p.K) break;
+            L = 0;
+            K = min(p.K - tb, C);
+            fold = K == C;
+            NE = K;
+            __syncthreads();  // every read of the last segment's LDS is done
+            load_tokens();
+            stage_tokens();
+            run_segment(std::false_type{});
         }
     }
 }
@@ -601,12 +634,18 @@ struct ChunkShape {
 // there run faster on them than on the vector ALUs from two tokens on; the
 // library sends a single token to the single-token kernel).  The 16 KB heads
 // of D = 64 and below stay on the vector ALUs.
-template <int OP, typename TIn, int D, int CMAX>
-hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
+template <int OP, typename TIn, int D, int CMAX, bool SEG>
+hipError_t launch_chunk_form(const ChunkParams &p, hipStream_t s) {
     constexpr int TV = ChunkShape<D>::TV, NT = ChunkShape<D>::NT;
     const unsigned blocks = (unsigned)p.N;
-    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, D == 128>), dim3(blocks), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, D == 128, SEG>), dim3(blocks), dim3(NT), 0, s, p);
     return hipGetLastError();
+}
+
+template <int OP, typename TIn, int D, int CMAX>
+hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
+    return p.segmented ? launch_chunk_form<OP, TIn, D, CMAX, true>(p, s)
+                       : launch_chunk_form<OP, TIn, D, CMAX, false>(p, s);
 }
 
 template <int OP, typename TIn, int D>

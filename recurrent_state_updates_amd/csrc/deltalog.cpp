@@ -393,41 +393,27 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     // one token: the single-token kernel is faster than a chunk of one
     if (K == 1) return dl_decode_step(h, &args[0], stream);
     if (h->slots) {
-        // Every slot's log fills at its own token.  Launch j takes segment j
-        // of each active slot's tokens: the first up to the slot's fold, then
-        // C at a time on an empty log.  The slots needing most segments set
-        // the number of launches.
-        const int C = h->cfg.C;
-        int nseg = 1;
-        for (int b = 0; b < h->cfg.B; ++b) {
-            const int room = C - slot_length(h, b);
-            if (h->h_active[b] && K > room) nseg = std::max(nseg, 1 + (K - room + C - 1) / C);
-        }
-        for (int seg = 0; seg < nseg; ++seg) {
-            dlk::ChunkParams p = chunk_of(0, K);
-            p.slot_base = h->slot_base;
-            p.slot_active = h->slot_active;
-            p.step = h->step;
-            p.seg = seg;
-            if ((st = launch_chunk(p)) != DL_OK) return st;
-        }
+        // Every slot's log fills at its own token: one segmented launch, in
+        // which each slot folds when its log fills and goes on from there.
+        dlk::ChunkParams p = chunk_of(0, K);
+        p.segmented = 1;
+        p.slot_base = h->slot_base;
+        p.slot_active = h->slot_active;
+        p.step = h->step;
+        if ((st = launch_chunk(p)) != DL_OK) return st;
         h->step += (unsigned)K;
         return DL_OK;
     }
-    for (int t0 = 0; t0 < K;) {
-        const int k1 = std::min(K - t0, h->cfg.C - h->L);  // the part that fits the log
-        if (k1 == 1) {
-            if ((st = dl_decode_step(h, &args[t0], stream)) != DL_OK) return st;
-            t0 += 1;
-            continue;
-        }
-        dlk::ChunkParams p = chunk_of(t0, k1);
-        p.L = h->L;
-        p.fold = h->L + k1 == h->cfg.C;
-        if ((st = launch_chunk(p)) != DL_OK) return st;
-        h->L = p.fold ? 0 : h->L + k1;
-        t0 += k1;
+    dlk::ChunkParams p = chunk_of(0, K);
+    p.L = h->L;
+    if (h->L + K > h->cfg.C) {
+        // the call passes the log's end: fold there and go on in the same launch
+        p.segmented = 1;
+    } else {
+        p.fold = h->L + K == h->cfg.C;
     }
+    if ((st = launch_chunk(p)) != DL_OK) return st;
+    h->L = (h->L + K) % h->cfg.C;
     return DL_OK;
 }
 

@@ -79,14 +79,14 @@ struct ChunkParams {
     int N;
     int K;     // tokens in the chunk, 1 <= K <= KMAX_TOKENS
     int fold;  // 1: L + K == C, fold every entry into the base
-    // per-slot handles (slot_base != NULL): each slot's log length is
-    // (step - slot_base[b]) mod C and L, fold are ignored; the launch takes
-    // segment seg of every active slot's K tokens (segment 0 runs up to the
-    // slot's fold, each later one holds up to C tokens on an empty log)
+    // segmented != 0: the K tokens may pass the log's end; the kernel folds
+    // when the log fills and starts an empty log for the rest (fold is then
+    // ignored).  Per-slot handles (slot_base != NULL) are always segmented:
+    // each slot's log length is (step - slot_base[b]) mod C, and L is ignored.
+    int segmented;
     const int *slot_base;
     const unsigned char *slot_active;
     unsigned step;
-    int seg;
 };
 
 hipError_t launch_gdn_chunk(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s);

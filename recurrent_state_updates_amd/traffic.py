@@ -85,15 +85,30 @@ def chunk_bytes(sh: Shape, L: int, K: int, fold: bool) -> int:
     return sh.heads * per + sh.shared()
 
 
-def multi_token_cycle_bytes(sh: Shape, C: int, K: int) -> int:
-    """One merge cycle of C tokens decoded K at a time (chunks split at C)."""
-    total, L = 0, 0
-    left = C
+def call_bytes(sh: Shape, L: int, K: int, C: int) -> int:
+    """K tokens in one launch from log length L, folding whenever the log
+    fills and going on from the base in registers: one read of the base, one
+    write per fold, every token in and out, the L old entries replayed, and
+    the entries of the last segment written unless it folds."""
+    per = sh.base()
+    left, l = K, L
     while left > 0:
-        k = min(K, C - L)
-        fold = L + k == C
-        total += chunk_bytes(sh, L, k, fold)
-        L = 0 if fold else L + k
+        k = min(left, C - l)
+        fold = l + k == C
+        per += k * (sh.token_in() + sh.out()) + l * sh.entry()
+        per += sh.base() if fold else k * sh.entry()
+        l = 0 if fold else l + k
+        left -= k
+    return sh.heads * per + sh.shared()
+
+
+def multi_token_bytes(sh: Shape, C: int, K: int, ntokens: int, L: int = 0) -> int:
+    """ntokens tokens decoded in calls of K from log length L."""
+    total, left = 0, ntokens
+    while left > 0:
+        k = min(K, left)
+        total += call_bytes(sh, L, k, C)
+        L = (L + k) % C
         left -= k
     return total
 

@@ -50,3 +50,26 @@ def test_rejects_invalid():
         dl.dl_choose_capacity(dl.make_config("gdn", "bf16", 1, 1, 128, 128, 8), 33)
     with pytest.raises(dl.DeltaLogError):
         dl.dl_choose_capacity(dl.make_config("gdn", "bf16", 1, 1, 128, 128, 8), 0)
+
+
+def test_call_bytes_of_segmented_launches():
+    """A call that fits the log moves what one chunk moves; a call that passes
+    the log's end moves the chunks it splits into, less the base reads that
+    the later segments take from registers."""
+    from recurrent_state_updates_amd import traffic as T
+    for op, d, s in (("gdn", 128, 2), ("kda", 64, 4), ("rwkv6", 32, 2)):
+        sh = T.Shape(op, 3, 2, d, s)
+        for C in (4, 8, 13):
+            for L in range(C):
+                for K in range(1, 9):
+                    got = T.call_bytes(sh, L, K, C)
+                    parts, l, left = [], L, K
+                    while left > 0:
+                        k = min(left, C - l)
+                        parts.append(T.chunk_bytes(sh, l, k, l + k == C))
+                        l = 0 if l + k == C else l + k
+                        left -= k
+                    want = sum(parts) - (len(parts) - 1) * (sh.heads * sh.base() + sh.shared())
+                    assert got == want, (op, C, L, K)
+    sh = T.Shape("gdn", 128, 32, 128, 2)
+    assert T.multi_token_bytes(sh, 8, 8, 16) == 2 * T.chunk_bytes(sh, 0, 8, True)

@@ -75,8 +75,8 @@ def parse():
     ap.add_argument("--no-eager", action="store_true", help="skip the eager GPU kernel")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the CPU-baseline sample")
     ap.add_argument("--report", default=None, help="also append the JSON line to this file")
-    ap.add_argument("--tokens", type=int, default=0,
-                    help="also time multi-token decode: K tokens per dl_decode_tokens call")
+    ap.add_argument("--tokens", type=int, default=8,
+                    help="also time multi-token decode: K tokens per dl_decode_tokens call (0: skip)")
     ap.add_argument("--staggered", action="store_true",
                     help="also time per-slot logs with slot b starting at token b mod C, so that "
                          "1/C of the slots fold at every step (continuous batching); with --tokens K "

@@ -7,7 +7,10 @@
 // log for each, and resolves the dependence of token t on the earlier tokens
 // of the chunk by a forward substitution over the value factors, column by
 // column.  The tokens are then appended to the log, or, when the chunk fills
-// it, the whole log is folded into the base with one read and one write.
+// it, the whole log is folded into the base with one read and one write.  If
+// the log fills before the call's last token (on a per-slot handle, at each
+// slot's own token), the fold leaves the new base in the registers and the
+// rest of the tokens run as a further segment on an empty log.
 //
 // Algebra (per head; g_t = g_L + sum_{m<=t} log2 decay_m, g_{-1} = g_L; the
 // reference point rho_t = g_t for the delta rules, g_{t-1} for RWKV6):
@@ -31,9 +34,9 @@ __device__ __forceinline__ void store_raw(bf16_bits *dst, float x) {
 }
 
 // Token pointers of the kernel arguments as opaque scalar values.  The lanes
-// of one wave belong to GPW consecutive key-side groups (tokens tb + t0 .. tb
-// + t0 + GPW - 1, tb and t0 uniform), so each lane chooses among GPW pointers, each a
-// scalar load at a uniform index.  Left visible, the choice would be folded
+// of one wave belong to GPW consecutive key-side groups (tokens tb + t0 ..
+// tb + t0 + GPW - 1, tb and t0 uniform), so each lane chooses among GPW
+// pointers, each a scalar load at a uniform index.  Left visible, the choice would be folded
 // back into an index into the argument array, read with a vector load that
 // the data load must wait for; the empty asm prevents that.  The result is
 // returned as a global-memory pointer (the asm hides where it came from).
@@ -65,9 +68,13 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
 // SEG runs every segment of the call in one workgroup: when the log fills
 // before the call's last token, the fold updates the register tile in place
 // and the rest of the tokens start an empty log from it (per-slot handles,
-// and calls that pass C).  Without SEG the chunk fits the log.
+// and calls that pass C).  Without SEG the chunk fits the log.  The
+// segmented matrix-core form at C <= 8 asks for three waves per SIMD, which
+// the compiler meets without spilling (left alone, KDA settles one register
+// above that, at two waves).
 template <int OP, typename TIn, int D, int TV, int NT, int CMAX, bool MM, bool SEG>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SEG && MM && CMAX == 8 ? 3 : 1))) void chunk_kernel(const ChunkParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SEG && MM && CMAX == 8 ? 3 : 1)))
+void chunk_kernel(const ChunkParams p) {
     using G = Geom<D, TV, NT>;
     constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
     constexpr int KL = G::KL, EPP = G::EPP;

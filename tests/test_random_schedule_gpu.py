@@ -80,3 +80,92 @@ def test_random_schedule(op, seed):
     eo = max(gs.rel(o[i], ref["out"][i]) for i in range(T))
     es = max(gs.rel(checks[s].numpy().reshape(Bsz * H, d, d), ref["states"][m]) for m, s in enumerate(steps))
     assert eo <= gs.OUT_GATE and es <= gs.STATE_GATE, (eo, es, Bsz, H, d, C, dtype, T, schedule)
+
+
+def _slot_reference(x, op, slot, start, end, S0_seg):
+    """Oracle of one slot's heads over tokens [start, end) from S0_seg [H, d, d]."""
+    sl = {key: (None if x[key] is None else x[key][start:end, slot:slot + 1])
+          for key in ("q", "k", "v", "beta", "decay")}
+    sl["bonus"] = x["bonus"]
+    sl["S0"] = S0_seg[None]
+    return gs.oracle_run(sl, op, chk_steps=[end - start])
+
+
+@pytest.mark.parametrize("op,seed", [(op, s) for op in ("gdn", "kda", "rwkv6") for s in range(3)])
+def test_random_slot_schedule(op, seed):
+    """Per-slot handles under a seeded random schedule: slots join and leave at
+    random tokens with fresh states, calls of 1 to 8 tokens find every slot at
+    its own log length (and fold some of them once or several times), and
+    whole-handle and single-slot early merges come in between.  Every active
+    slot's outputs and final state against the oracle of its own tokens."""
+    rng = np.random.default_rng(5000 * seed + {"gdn": 11, "kda": 12, "rwkv6": 13}[op])
+    Bsz, H = int(rng.integers(2, 6)), int(rng.integers(1, 3))
+    d = int(rng.choice([32, 64, 128]))
+    C = int(rng.choice([1, 2, 3, 5, 8, 11, 16]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    T = int(rng.integers(24, 40))
+    x = workloads.generate(op, Bsz, H, d, d, T, dtype, seed=9000 + seed)
+    dev = gs.to_device(x, DEV)
+    g = torch.Generator().manual_seed(300 + seed)
+    # each slot: one or two active segments [s, e)
+    segments = {}
+    for b in range(Bsz):
+        s0 = int(rng.integers(0, T // 2))
+        e0 = int(rng.integers(s0 + 1, T + 1))
+        segs = [(s0, e0)]
+        if e0 < T - 2 and rng.random() < 0.5:
+            s1 = int(rng.integers(e0 + 1, T))
+            segs.append((s1, T))
+        segments[b] = segs
+    seg_S0 = {(b, s): torch.randn((H, d, d), generator=g) * 0.02 for b, segs in segments.items()
+              for s, _ in segs}
+    events = sorted({t for segs in segments.values() for se in segs for t in se} | {T})
+    base = torch.zeros((Bsz, H, d, d), dtype=torch.float32, device=DEV)
+    st = dl.DeltaLogState(op, dtype, base, C, slots=True)
+    outs = torch.full((T, Bsz, H, d), float("nan"), dtype=torch.float32, device=DEV)
+    expect, t, schedule = {}, 0, []
+    while t < T:
+        for b, segs in segments.items():
+            for s, e in segs:
+                if e == t:
+                    st.deactivate(b)
+                    expect.pop(b, None)
+                if s == t:
+                    base[b].copy_(seg_S0[(b, s)].to(DEV))
+                    st.activate(b)
+                    expect[b] = 0
+        r = rng.random()
+        if r < 0.1 and expect:
+            st.merge()
+            expect = {b: 0 for b in expect}
+            schedule.append("merge")
+        elif r < 0.2 and expect:
+            b = int(rng.choice(sorted(expect)))
+            st.merge_slot(b)
+            expect[b] = 0
+            schedule.append(f"merge_slot{b}")
+        nxt = next(e for e in events if e > t)
+        t1 = min(t + int(rng.integers(1, dl.DL_MAX_TOKENS + 1)), nxt)
+        st.step_tokens(out=outs[t:t1], **_chunk_tokens(dev, t, t1))
+        schedule.append(f"call{t1 - t}")
+        for b in expect:
+            expect[b] = (expect[b] + t1 - t) % C
+        for b in range(Bsz):
+            assert st.slot_log_length(b) == expect.get(b, -1), (t1, b, schedule)
+        t = t1
+    final = st.materialize(torch.full_like(base, float("nan")))
+    torch.cuda.synchronize()
+    o = outs.cpu().numpy()
+    fin = final.cpu().numpy()
+    for b, segs in segments.items():
+        active = np.zeros(T, dtype=bool)
+        for s, e in segs:
+            active[s:e] = True
+            ref = _slot_reference(x, op, b, s, e, seg_S0[(b, s)])
+            worst = max(gs.rel(o[s + j, b], ref["out"][j]) for j in range(e - s))
+            assert worst <= gs.OUT_GATE, (b, s, e, worst, d, C, dtype, schedule)
+            if e == T:
+                assert gs.rel(fin[b], ref["states"][0]) <= gs.STATE_GATE, (b, d, C, dtype, schedule)
+        assert np.isnan(o[~active, b]).all()
+        if not active[-1]:
+            assert np.isnan(fin[b]).all()

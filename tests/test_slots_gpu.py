@@ -243,7 +243,7 @@ def test_tokens_on_a_per_slot_handle_equal_single_steps(op):
 CHUNK_CASES = [("gdn", "bf16", 128, 8), ("kda", "bf16", 128, 4), ("rwkv6", "bf16", 64, 8),
                ("gdn", "f32", 32, 3), ("kda", "f32", 64, 13), ("rwkv6", "bf16", 128, 5),
                ("gdn", "f32", 128, 6), ("kda", "f32", 128, 8), ("rwkv6", "f32", 128, 8),
-               ("kda", "bf16", 128, 16), ("gdn", "bf16", 128, 32)]
+               ("kda", "bf16", 128, 16), ("gdn", "bf16", 128, 32), ("gdn", "bf16", 64, 1)]
 
 
 @pytest.mark.parametrize("op,dtype,d,C", CHUNK_CASES)

@@ -326,7 +326,7 @@ def main():
         del src, dst
 
     if args.cold:
-        result["cold"] = cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs)
+        result["cold"] = cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, args.tokens)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(x, w, Bsz, args.cpu_tokens)
@@ -534,7 +534,7 @@ def staggered_multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs
             "achieved_GBps": round(nbytes / ntoks / (wall_us * 1e-6) / 1e9, 1)}
 
 
-def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs):
+def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, ntok=0):
     """Per-launch event times with a 512 MB read between launches, outside the
     events: the read refills the 256 MB Infinity Cache with clean lines of
     another buffer, so each launch finds none of its data cached (a write
@@ -565,10 +565,40 @@ def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs):
             tok += 1
     st.close()
     per_tok = float(np.median(lat.sum(axis=1))) / C
-    return {"us_per_token": round(per_tok, 3),
-            "achieved_GBps": round(traffic.per_token_bytes(sh, C) / (per_tok * 1e-6) / 1e9, 1),
-            "append_by_L": [round(float(np.median(lat[:, L])), 2) for L in range(C - 1)],
-            "decode_fold": round(float(np.median(lat[:, C - 1])), 2)}
+    result = {"us_per_token": round(per_tok, 3),
+              "achieved_GBps": round(traffic.per_token_bytes(sh, C) / (per_tok * 1e-6) / 1e9, 1),
+              "append_by_L": [round(float(np.median(lat[:, L])), 2) for L in range(C - 1)],
+              "decode_fold": round(float(np.median(lat[:, C - 1])), 2)}
+    if ntok > 1:
+        # the same for calls of ntok tokens, one launch each.  As above, the
+        # refill is queued ahead of the first event without waiting, so that
+        # the host has issued the launch by the time the refill ends.
+        base = d["S0"].clone()
+        st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
+        fn = dl.load_library().dl_decode_tokens
+        one = [st.step_args(d["q"][t], d["k"][t], d["v"][t], None if d["beta"] is None else d["beta"][t],
+                            d["decay"][t], d["bonus"], outs[t]) for t in range(w.T)]
+        ncalls = max(4, ncyc * C // ntok)
+        lat_mt, tok, L = [], 0, 0
+        nbytes = 0
+        for _ in range(ncalls):
+            arr = (dl.StepArgs * ntok)(*[one[(tok + i) % w.T] for i in range(ntok)])
+            torch.sum(flush, dim=0, out=sink)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert fn(st.handle, arr, ntok, stream.cuda_stream) == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            lat_mt.append(e0.elapsed_time(e1) * 1e3)
+            nbytes += traffic.call_bytes(sh, L, ntok, C)
+            L = (L + ntok) % C
+            tok += ntok
+        st.close()
+        per_tok_mt = sum(lat_mt) / (ncalls * ntok)
+        result["multi_token"] = {"tokens_per_call": ntok, "us_per_token": round(per_tok_mt, 3),
+                                 "achieved_GBps": round(nbytes / (ncalls * ntok) / (per_tok_mt * 1e-6) / 1e9, 1)}
+    return result
 
 
 def cpu_baseline(x, w, Bsz, tokens):

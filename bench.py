@@ -627,9 +627,16 @@ def cpu_baseline(x, w, Bsz, tokens):
     t0 = time.perf_counter()
     oracle.eager_run(w.op, q, k, v, beta, decay, bonus, S0, nthreads=threads)
     wall = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": round(wall * 1e6 / T, 1), "unit": "us/token", "cores": threads, "kind": "oracle",
             "sample": f"all {N} heads of {w.name} (B={Bsz}), first {T} tokens, fp64, "
-                      f"{threads} threads; wall {wall:.2f} s"}
+                      f"{threads} threads; wall {wall:.2f} s",
+            "cpu_model": model, "host_cpus_available": ncpu}
 
 
 if __name__ == "__main__":

@@ -306,3 +306,36 @@ def test_continuous_batching_in_chunks(op, dtype, d, C):
             active[s:e] = True
         assert np.isnan(o[~active, b]).all()
     assert np.isnan(fin[3]).all()
+
+
+def test_full_size_staggered_calls_of_eight():
+    """The staggered serving shape the multi-token bench times: GDN B=128 H=32
+    d=128 C=8, slot b started at token b mod 8 (single steps while the slots
+    join), then calls of eight tokens, every call folding seven slots in eight
+    in its middle.  Eight sampled slots (all their heads): every output and the
+    final state against the oracle of each slot's own tokens."""
+    w = workloads.WORKLOADS["gdn_b128_h32_d128"]
+    T, C = 32, 8
+    x = workloads.generate_workload(w, T=T)
+    dev = gs.to_device(x, DEV)
+    base = dev["S0"].clone()
+    st = dl.DeltaLogState("gdn", w.in_dtype, base, C, slots=True)
+    outs = torch.full((T, w.B, w.H, w.d), float("nan"), dtype=torch.float32, device=DEV)
+    for t in range(C):
+        for b in range(t, w.B, C):
+            st.activate(b)
+        st.step(out=outs[t], **_token(dev, t))
+    for t0 in range(C, T, 8):
+        tok = {k: (v if v is None or k == "bonus" else v[t0:t0 + 8]) for k, v in dev.items()
+               if k in ("q", "k", "v", "beta", "decay", "bonus")}
+        st.step_tokens(out=outs[t0:t0 + 8], **tok)
+    final = st.materialize()
+    torch.cuda.synchronize()
+    for b in (0, 1, 6, 7, 63, 64, 121, 127):
+        s = b % C
+        ref = _segment_reference(x, "gdn", b, w.H, s, T, x["S0"][b], chk_end=True)
+        o = outs[s:, b].cpu().numpy()
+        worst = max(gs.rel(o[j], ref["out"][j]) for j in range(T - s))
+        assert worst <= gs.OUT_GATE, (b, worst)
+        assert gs.rel(final[b].cpu().numpy(), ref["states"][0]) <= gs.STATE_GATE, b
+        assert np.isnan(outs[:s, b].cpu().numpy()).all()

@@ -27,7 +27,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, vendor figure
-METRIC = "amortized µs/token + achieved HBM GB/s, GDN B=128 H=32 d=128 C=8"
+METRIC_TEMPLATE = "amortized µs/token + achieved HBM GB/s, {op} B={B} H={H} d={d} C={C}"
+
+
+def metric_name(op, B, H, dk, dv, C):
+    """The metric string of the workload actually run (the headline run, GDN
+    B=128 H=32 d=128 C=8, gives the headline metric's exact name)."""
+    d = str(dk) if dk == dv else f"{dk}x{dv}"
+    return METRIC_TEMPLATE.format(op=op.upper(), B=B, H=H, d=d, C=C)
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "append_gdn_b128_h32_d128_c8_traffic.md")
 KERNEL_SOURCES = ["recurrent_state_updates_amd/csrc/step_kernel.h",
                   "recurrent_state_updates_amd/csrc/launch.h"]
@@ -210,7 +219,7 @@ def main():
     measured = measured_traffic(dom_bytes) if (w.name == "gdn_b128_h32_d128" and C == 8 and Bsz == 128) else None
 
     result = {
-        "metric": METRIC,
+        "metric": metric_name(w.op, Bsz, H, D, D, C),
         "value": round(us_per_token, 3),
         "unit": "us/token",
         "n_gpus": 1,

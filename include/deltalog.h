@@ -32,8 +32,16 @@
  *    must be aligned to four elements (8 bytes in bf16, 16 in f32), and the
  *    per-channel decay (KDA, RWKV6) and the bonus as float4, so those must
  *    be 16-byte aligned; every other device pointer must be aligned to its
- *    element size.  Buffers named as outputs must not overlap inputs unless
- *    stated.
+ *    element size.
+ *  - Aliasing (checked on byte ranges, DL_ERR_ARG): the base and the
+ *    workspace are disjoint; a token's out overlaps none of its inputs; no
+ *    input or output of a token overlaps the base, the workspace or the
+ *    prep buffer of the handle (every launch may write them); the tokens of
+ *    one dl_decode_tokens call write disjoint outputs that overlap no
+ *    token's inputs; a materialise dst overlaps none of the base, the
+ *    workspace and the prep buffer; the prep buffer overlaps neither the
+ *    base nor the workspace; for dl_eager_step no input or output overlaps
+ *    the state.
  *  - Return values are dl_status codes: DL_OK (0) or a negative error.  Every
  *    argument is checked before anything is enqueued, so on any error but
  *    DL_ERR_HIP nothing was enqueued and the handle is unchanged;
@@ -110,9 +118,13 @@ typedef struct {
 
 typedef struct dl_state dl_state; /* opaque, host memory only */
 
-/* Bytes of device workspace holding the log of capacity C for cfg (value
- * factors, key copies and cumulative log-decays; see dl_workspace_layout).
- * Returns 0 for an invalid or unsupported cfg. */
+/* Bytes of device workspace holding the bounded update log of capacity C
+ * for cfg: per head, up to C compact update factors and their log-decay
+ * metadata (gist.science summary, "Meccanismo Core: Base + Log": the
+ * bounded update log beside the dense base), i.e. O(C (dk + dv)) numbers
+ * against the dk * dv of the state ("Problema": a token contributes
+ * O(dk + dv)).  Value factors, key copies and cumulative log-decays; see
+ * dl_workspace_layout.  Returns 0 for an invalid or unsupported cfg. */
 size_t dl_workspace_bytes(const dl_config *cfg);
 
 /* Byte offsets inside the workspace of its three arrays, for inspection:
@@ -124,10 +136,15 @@ size_t dl_workspace_bytes(const dl_config *cfg);
  * error for an invalid cfg or a NULL offsets. */
 dl_status dl_workspace_layout(const dl_config *cfg, size_t offsets[3]);
 
-/* Create a handle over a caller-owned base state and workspace.
+/* Create a handle over a caller-owned base state and workspace: the dense
+ * base, the history up to the last merge, and the bounded log of recent
+ * compact factors beside it (gist.science summary, "Meccanismo Core: Base +
+ * Log"); the state of each head is a dk x dv matrix and the layer's a
+ * [B,H,dk,dv] tensor ("Problema").
  *   base       [B,H,dk,dv] fp32 device memory holding the current dense state
  *              (the initial state, or a state saved after a fold: resume)
- *   workspace  device memory of at least dl_workspace_bytes(cfg) bytes
+ *   workspace  device memory of at least dl_workspace_bytes(cfg) bytes,
+ *              disjoint from the base
  * The log starts empty (L = 0); no device work is done.  *out receives the
  * handle (NULL on error).  The buffers must outlive the handle. */
 dl_status dl_state_init(dl_state **out, const dl_config *cfg, float *base,
@@ -156,16 +173,26 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *args, void *stream);
  * representation (gist.science summary, "Meccanismo Core: Base + Log"). */
 dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *stream);
 
-/* Fold the current log into the base now (an early merge), L becomes 0.
- * Output-neutral: later outputs are unchanged.  A no-op when L == 0. */
+/* Fold the current log into the base now, L becomes 0: the merge phase
+ * (gist.science summary, "Fase di Merge": the accumulated logical state,
+ * base plus replayed log entries, is written back into the dense base and
+ * the log is reset), taken before the log is full.  dl_decode_step runs the
+ * same fold by itself when a token fills the log.  Output-neutral: later
+ * outputs are unchanged.  A no-op when L == 0. */
 dl_status dl_merge(dl_state *h, void *stream);
 
 /* Write the logical dense state [B,H,dk,dv] fp32 into dst without changing
- * the handle, the base or the log.  dst must not be the base. */
+ * the handle, the base or the log: the state eager decoding would hold
+ * after the same tokens (the signal-papers summary, Fig. 4: the logical
+ * state that a merge materialises into the base; Fig. 12 (b): the
+ * materialised recurrent state whose relative error the pages report).
+ * dst must overlap none of the base, the workspace and the prep buffer
+ * (DL_ERR_ARG). */
 dl_status dl_materialize(const dl_state *h, float *dst, void *stream);
 
-/* Current log length L in [0, C) of a lockstep handle; -1 for a NULL or a
- * per-slot handle (see dl_slot_log_length). */
+/* Current log length L in [0, C) of a lockstep handle -- the L of the
+ * signal-papers summary, Fig. 4 (append while L < C, materialise when
+ * L = C) -- or -1 for a NULL or a per-slot handle (see dl_slot_log_length). */
 int dl_log_length(const dl_state *h);
 
 /* Split replay (the pages' staged kernel: gist.science summary, "Implementazione
@@ -249,9 +276,10 @@ int dl_slot_log_length(const dl_state *h, int slot);
 
 /* Write the logical state of one slot, [H,dk,dv] fp32, into dst (for
  * example to save a request that leaves); nothing else changes.  Lockstep
- * and per-slot handles; one launch over the slot's H heads only.  dst must
- * not overlap the slot's base block.  DL_ERR_ARG for a bad slot, an inactive
- * slot of a per-slot handle, or a bad dst. */
+ * and per-slot handles; one launch over the slot's H heads only.
+ * DL_ERR_ARG for a bad slot, an inactive
+ * slot of a per-slot handle, or a dst that overlaps the base, the workspace
+ * or the prep buffer. */
 dl_status dl_materialize_slot(const dl_state *h, int slot, float *dst, void *stream);
 
 /* Fold one active slot's log into its base block now (an early merge of that

@@ -61,24 +61,46 @@ RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
 
 
 def check_resources(src, lines):
-    """Raise if a kernel of ``src`` spills VGPRs or uses per-lane scratch."""
-    fn, bad = None, []
+    """Raise if a kernel of ``src`` spills VGPRs or uses per-lane scratch.
+
+    Every kernel's remark block must be present and complete: a source that
+    yields no block, or a block without both the spill count and the scratch
+    size, stops the build too (a toolchain that renamed the fields or stopped
+    forwarding the remarks would otherwise pass the guard without checking
+    anything).  Returns {kernel: {field: value}} for the blocks found."""
+    blocks, fn = {}, None
     for ln in lines:
         m = re.search(r"Function Name: (\S+)", ln)
         if m:
             fn = m.group(1)
+            blocks.setdefault(fn, {})
             continue
-        m = re.search(r"(VGPRs Spill|ScratchSize \[bytes/lane\]): (\d+)", ln)
-        if m and int(m.group(2)) > 0:
-            bad.append(f"{fn}: {m.group(1)} {m.group(2)}")
+        m = re.search(r"(VGPRs Spill|ScratchSize \[bytes/lane\]|VGPRs|Occupancy \[waves/SIMD\]): (\d+)", ln)
+        if m and fn is not None:
+            blocks[fn][m.group(1)] = int(m.group(2))
+    if not blocks:
+        raise RuntimeError(f"{src}: the compiler printed no kernel resource remarks; "
+                           "the no-spill guard cannot check this source")
+    incomplete = [k for k, f in blocks.items() if "VGPRs Spill" not in f or "ScratchSize [bytes/lane]" not in f]
+    if incomplete:
+        raise RuntimeError(f"{src}: resource remarks without a spill count or a scratch size for:\n"
+                           + "\n".join(incomplete))
+    bad = [f"{k}: VGPRs Spill {f['VGPRs Spill']}, ScratchSize {f['ScratchSize [bytes/lane]']}"
+           for k, f in blocks.items() if f["VGPRs Spill"] > 0 or f["ScratchSize [bytes/lane]"] > 0]
     if bad:
         raise RuntimeError(f"{src}: kernels that spill to scratch are not built:\n" + "\n".join(bad))
+    return blocks
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
     """Compile and link the library; returns its path."""
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
+    # a refused or failed build leaves no library behind to be loaded
+    tmp = LIB + ".tmp"
+    for path in (LIB, tmp):
+        if os.path.exists(path):
+            os.remove(path)
     objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
@@ -90,7 +112,6 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src, lines in outs:
         if src.endswith(".hip"):
             check_resources(src, lines)
-    tmp = LIB + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB

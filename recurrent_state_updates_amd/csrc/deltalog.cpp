@@ -41,6 +41,9 @@ struct dl_state {
     unsigned step;
     // split replay: per-head prep records (NULL: the fused per-tile preparation)
     float *prep;
+    // byte ranges the handle's launches write: the base, the part of the
+    // workspace the kernels use, the prep records (empty when unset)
+    uintptr_t base_lo, base_hi, ws_lo, ws_hi, prep_lo, prep_hi;
 };
 
 // A merge cycle captured for replay (dl_graph_capture_cycle).
@@ -59,6 +62,24 @@ dl_status fail(dl_status st, const std::string &msg) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A byte range [lo, hi) of device memory; a NULL pointer is an empty range.
+struct Span {
+    uintptr_t lo, hi;
+};
+
+Span span(const void *p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return p ? Span{a, a + bytes} : Span{0, 0};
+}
+
+bool overlap(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+// A buffer a call writes, by name, for the messages.
+struct Written {
+    Span s;
+    const char *name;
+};
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -104,6 +125,52 @@ Layout layout_of(const dl_config *cfg, size_t heads) {
     return l;
 }
 
+// The byte ranges of one token's inputs ([0] q, [1] k, [2] v, [3] beta,
+// [4] decay, [5] bonus) and of its output.
+struct TokenSpans {
+    Span in[6];
+    Span out;
+};
+
+TokenSpans token_spans(const dl_config *cfg, const dl_step_args *a) {
+    const size_t n = (size_t)cfg->B * (size_t)cfg->H, es = in_size(cfg->in_dtype);
+    TokenSpans t;
+    t.in[0] = span(a->q, n * cfg->dk * es);
+    t.in[1] = span(a->k, n * cfg->dk * es);
+    t.in[2] = span(a->v, n * cfg->dv * es);
+    t.in[3] = span(a->beta, n * 4);
+    t.in[4] = span(a->decay, (cfg->op == DL_GDN ? n : n * cfg->dk) * 4);
+    t.in[5] = span(a->bonus, (size_t)cfg->H * cfg->dk * 4);
+    t.out = span(a->out, n * cfg->dv * 4);
+    return t;
+}
+
+// No aliasing a launch could race on: the token's output overlaps none of its
+// inputs, and neither overlaps a buffer the call writes.
+dl_status check_token_aliasing(const dl_config *cfg, const dl_step_args *a, const Written *w, int nw) {
+    static const char *in_names[6] = {"q", "k", "v", "beta", "decay", "bonus"};
+    const TokenSpans t = token_spans(cfg, a);
+    for (int i = 0; i < 6; ++i)
+        if (overlap(t.out, t.in[i]))
+            return fail(DL_ERR_ARG, std::string("out overlaps the token's input ") + in_names[i]);
+    for (int j = 0; j < nw; ++j) {
+        if (overlap(t.out, w[j].s)) return fail(DL_ERR_ARG, std::string("out overlaps the ") + w[j].name);
+        for (int i = 0; i < 6; ++i)
+            if (overlap(t.in[i], w[j].s))
+                return fail(DL_ERR_ARG, std::string("input ") + in_names[i] + " overlaps the " + w[j].name +
+                                            ", which the call writes");
+    }
+    return DL_OK;
+}
+
+// The buffers a handle's decode, merge and materialise launches write.
+int handle_written(const dl_state *h, Written w[3]) {
+    w[0] = {Span{h->base_lo, h->base_hi}, "base"};
+    w[1] = {Span{h->ws_lo, h->ws_hi}, "workspace"};
+    w[2] = {Span{h->prep_lo, h->prep_hi}, "prep buffer"};
+    return 3;
+}
+
 dl_status check_args(const dl_config *cfg, const dl_step_args *a) {
     if (!a) return fail(DL_ERR_ARG, "args is NULL");
     if (!a->q || !a->k || !a->v || !a->decay || !a->out)
@@ -128,6 +195,15 @@ dl_status check_args(const dl_config *cfg, const dl_step_args *a) {
     for (const void *p : f32_ptrs)
         if (addr(p) % 4 != 0) return fail(DL_ERR_ARG, "beta, decay and out must be 4-byte aligned");
     return DL_OK;
+}
+
+// check_args plus the aliasing rules against a handle's buffers.
+dl_status check_step(const dl_state *h, const dl_step_args *a) {
+    dl_status st = check_args(&h->cfg, a);
+    if (st != DL_OK) return st;
+    Written w[3];
+    const int nw = handle_written(h, w);
+    return check_token_aliasing(&h->cfg, a, w, nw);
 }
 
 dl_status launch(const dl_config *cfg, int mode, const dlk::StepParams &p, void *stream) {
@@ -203,6 +279,9 @@ dl_status init_handle(dl_state **out, const dl_config *cfg, float *base, void *w
     if (workspace_bytes < l.total)
         return fail(DL_ERR_WORKSPACE, "workspace is smaller than dl_workspace_bytes(cfg) = " +
                                           std::to_string(l.total));
+    const Span sb = span(base, heads * (size_t)cfg->dk * (size_t)cfg->dv * 4);
+    const Span sw = span(workspace, l.total);
+    if (overlap(sb, sw)) return fail(DL_ERR_ARG, "base and workspace overlap");
     dl_state *h = new (std::nothrow) dl_state;
     if (!h) return fail(DL_ERR_ARG, "out of host memory");
     char *ws = static_cast<char *>(workspace);
@@ -217,6 +296,11 @@ dl_status init_handle(dl_state **out, const dl_config *cfg, float *base, void *w
     h->slot_active = reinterpret_cast<unsigned char *>(ws + l.sa);
     h->step = 0;
     h->prep = nullptr;
+    h->base_lo = sb.lo;
+    h->base_hi = sb.hi;
+    h->ws_lo = sw.lo;
+    h->ws_hi = sw.hi;
+    h->prep_lo = h->prep_hi = 0;
     if (slots) {
         h->h_base.assign(cfg->B, 0u);
         h->h_active.assign(cfg->B, 0);
@@ -312,7 +396,7 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
     size_t heads = 0;
     dl_status st = check_config(&h->cfg, &heads);
     if (st != DL_OK) return st;
-    st = check_args(&h->cfg, a);
+    st = check_step(h, a);
     if (st != DL_OK) return st;
     dlk::StepParams p = params_of(&h->cfg, heads);
     set_log(p, h);
@@ -348,7 +432,21 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     if (!args) return fail(DL_ERR_ARG, "args is NULL");
     if (K < 1 || K > DL_MAX_TOKENS) return fail(DL_ERR_SHAPE, "K must lie in [1, 8]");
     for (int t = 0; t < K; ++t)
-        if ((st = check_args(&h->cfg, &args[t])) != DL_OK) return st;
+        if ((st = check_step(h, &args[t])) != DL_OK) return st;
+    // one launch reads every token's inputs and writes every token's output:
+    // no output may overlap another token's inputs or output
+    for (int t = 0; t < K; ++t) {
+        const TokenSpans ts = token_spans(&h->cfg, &args[t]);
+        for (int u = 0; u < K; ++u) {
+            if (u == t) continue;
+            const TokenSpans us = token_spans(&h->cfg, &args[u]);
+            if (overlap(ts.out, us.out))
+                return fail(DL_ERR_ARG, "two tokens of the call write overlapping outputs");
+            for (const Span &in : us.in)
+                if (overlap(ts.out, in))
+                    return fail(DL_ERR_ARG, "a token's out overlaps another token's input");
+        }
+    }
     // the bonus is a per-head parameter: one launch takes it from the first token
     for (int t = 1; t < K; ++t)
         if (args[t].bonus != args[0].bonus)
@@ -450,10 +548,17 @@ dl_status dl_materialize(const dl_state *h, float *dst, void *stream) {
     if (!h) return fail(DL_ERR_ARG, "handle is NULL");
     if (!dst) return fail(DL_ERR_ARG, "dst is NULL");
     if (!aligned16(dst)) return fail(DL_ERR_ARG, "dst must be 16-byte aligned");
-    if (dst == h->base) return fail(DL_ERR_ARG, "dst must not be the base (use dl_merge)");
     size_t heads = 0;
     dl_status st = check_config(&h->cfg, &heads);
     if (st != DL_OK) return st;
+    // the launch reads the base, the log and (never) the prep records while
+    // its workgroups write dst: dst must overlap none of them
+    const Span sd = span(dst, heads * (size_t)h->cfg.dk * (size_t)h->cfg.dv * 4);
+    Written w[3];
+    const int nw = handle_written(h, w);
+    for (int j = 0; j < nw; ++j)
+        if (overlap(sd, w[j].s))
+            return fail(DL_ERR_ARG, std::string("dst overlaps the ") + w[j].name + " (use dl_merge to fold in place)");
     dlk::StepParams p = params_of(&h->cfg, heads);
     set_log(p, h);
     p.dst = dst;
@@ -491,8 +596,11 @@ dl_status dl_materialize_slot(const dl_state *h, int slot, float *dst, void *str
     if (!dst) return fail(DL_ERR_ARG, "dst is NULL");
     if (!aligned16(dst)) return fail(DL_ERR_ARG, "dst must be 16-byte aligned");
     const size_t blk = (size_t)h->cfg.H * (size_t)h->cfg.dk * (size_t)h->cfg.dv;
-    const float *b0 = h->base + (size_t)slot * blk;
-    if (dst < b0 + blk && b0 < dst + blk) return fail(DL_ERR_ARG, "dst must not overlap the slot's base");
+    const Span sd = span(dst, blk * 4);
+    Written w[3];
+    const int nw = handle_written(h, w);
+    for (int j = 0; j < nw; ++j)
+        if (overlap(sd, w[j].s)) return fail(DL_ERR_ARG, std::string("dst overlaps the ") + w[j].name);
     if (h->slots && !h->h_active[slot]) return fail(DL_ERR_ARG, "slot is not active");
     return launch(&h->cfg, dlk::MODE_FOLD, slot_fold_params(h, slot, dst), stream);
 }
@@ -523,13 +631,19 @@ dl_status dl_set_split_replay(dl_state *h, void *prep, size_t prep_bytes) {
     if (h->slots) return fail(DL_ERR_UNSUPPORTED, "split replay needs a lockstep handle");
     if (!prep) {
         h->prep = nullptr;
+        h->prep_lo = h->prep_hi = 0;
         return DL_OK;
     }
     if (!aligned16(prep)) return fail(DL_ERR_ARG, "prep must be 16-byte aligned");
     const size_t need = dl_prep_bytes(&h->cfg);
     if (prep_bytes < need)
         return fail(DL_ERR_WORKSPACE, "prep is smaller than dl_prep_bytes(cfg) = " + std::to_string(need));
+    const Span sp = span(prep, need);
+    if (overlap(sp, Span{h->base_lo, h->base_hi}) || overlap(sp, Span{h->ws_lo, h->ws_hi}))
+        return fail(DL_ERR_ARG, "prep overlaps the base or the workspace");
     h->prep = static_cast<float *>(prep);
+    h->prep_lo = sp.lo;
+    h->prep_hi = sp.hi;
     return DL_OK;
 }
 
@@ -542,7 +656,7 @@ dl_status dl_graph_capture_cycle(dl_graph **out, dl_state *h, const dl_step_args
     if (!args) return fail(DL_ERR_ARG, "args is NULL");
     dl_status st;
     for (int t = 0; t < h->cfg.C; ++t)
-        if ((st = check_args(&h->cfg, &args[t])) != DL_OK) return st;
+        if ((st = check_step(h, &args[t])) != DL_OK) return st;
     hipStream_t cs = nullptr;
     hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
     if (e != hipSuccess) return fail(DL_ERR_HIP, std::string("hipStreamCreate: ") + hipGetErrorString(e));
@@ -599,6 +713,8 @@ dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *
     if (!aligned16(state)) return fail(DL_ERR_ARG, "state must be 16-byte aligned");
     st = check_args(cfg, a);
     if (st != DL_OK) return st;
+    const Written w = {span(state, heads * (size_t)cfg->dk * (size_t)cfg->dv * 4), "state"};
+    if ((st = check_token_aliasing(cfg, a, &w, 1)) != DL_OK) return st;
     dlk::StepParams p = params_of(cfg, heads);
     set_token(p, a);
     p.base = state;

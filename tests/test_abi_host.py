@@ -18,6 +18,12 @@ from recurrent_state_updates_amd import build as dlbuild
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "deltalog.h")
 FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
+# a fake device layout with no two buffers overlapping: the base at FAKE, the
+# workspace, the token inputs 1 MB apart, the prep records, a materialise dst
+WS = FAKE + 0x10000000
+IN = FAKE + 0x20000000
+PREP = FAKE + 0x30000000
+DST = FAKE + 0x40000000
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -104,8 +110,11 @@ def test_state_init_validation_and_bookkeeping():
         dl.dl_state_init(cfg, FAKE, FAKE, need - 1)
     assert ei.value.status == B.DL_ERR_WORKSPACE
     lib = B.load_library()
-    assert lib.dl_state_init(None, ctypes.byref(cfg), FAKE, FAKE, need) == B.DL_ERR_ARG
-    h = dl.dl_state_init(cfg, FAKE, FAKE, need)
+    assert lib.dl_state_init(None, ctypes.byref(cfg), FAKE, WS, need) == B.DL_ERR_ARG
+    with pytest.raises(dl.DeltaLogError) as ei:  # the workspace starts inside the base
+        dl.dl_state_init(cfg, FAKE, FAKE + 0x1000, need)
+    assert ei.value.status == B.DL_ERR_ARG
+    h = dl.dl_state_init(cfg, FAKE, WS, need)
     try:
         assert dl.dl_log_length(h) == 0
         dl.dl_merge(h)  # L == 0: a no-op, nothing is launched
@@ -116,33 +125,39 @@ def test_state_init_validation_and_bookkeeping():
         with pytest.raises(dl.DeltaLogError):
             dl.dl_materialize(h, 0)
         with pytest.raises(dl.DeltaLogError):
-            dl.dl_materialize(h, FAKE + 0x1000 + 8)
+            dl.dl_materialize(h, DST + 8)
     finally:
         dl.dl_state_destroy(h)
     assert dl.dl_log_length(None) == -1
     dl.dl_state_destroy(None)
 
 
+MB = 0x100000
+
+
 def _args(**over):
-    a = dict(q=FAKE, k=FAKE + 0x100, v=FAKE + 0x200, beta=FAKE + 0x300, decay=FAKE + 0x400,
-             bonus=0, out=FAKE + 0x500)
+    a = dict(q=IN, k=IN + MB, v=IN + 2 * MB, beta=IN + 3 * MB, decay=IN + 4 * MB, bonus=0, out=IN + 5 * MB)
     a.update(over)
     return B.StepArgs(**a)
 
 
 @pytest.mark.parametrize("op,over", [
     ("gdn", dict(q=0)), ("gdn", dict(out=0)), ("gdn", dict(decay=0)), ("gdn", dict(beta=0)),
-    ("gdn", dict(bonus=FAKE + 0x600)), ("kda", dict(beta=0)),
+    ("gdn", dict(bonus=IN + 6 * MB)), ("kda", dict(beta=0)),
     ("rwkv6", dict()),  # beta given, bonus missing
     ("rwkv6", dict(beta=0)),  # bonus missing
-    ("gdn", dict(k=FAKE + 0x101)), ("gdn", dict(out=FAKE + 0x502)), ("gdn", dict(beta=FAKE + 0x302)),
+    ("gdn", dict(k=IN + MB + 1)), ("gdn", dict(out=IN + 5 * MB + 2)), ("gdn", dict(beta=IN + 3 * MB + 2)),
     # q and k are read four channels at a time, per-channel decays and the bonus as float4
-    ("gdn", dict(q=FAKE + 2)), ("kda", dict(k=FAKE + 0x104)), ("gdn", dict(v=FAKE + 0x201)),
-    ("kda", dict(decay=FAKE + 0x404)), ("rwkv6", dict(beta=0, bonus=FAKE + 0x608)),
+    ("gdn", dict(q=IN + 2)), ("kda", dict(k=IN + MB + 4)), ("gdn", dict(v=IN + 2 * MB + 1)),
+    ("kda", dict(decay=IN + 4 * MB + 4)), ("rwkv6", dict(beta=0, bonus=IN + 6 * MB + 8)),
+    # aliasing: the output over an input, an input or the output over the base or the log
+    ("gdn", dict(out=IN + 2 * MB + 0x100)), ("kda", dict(out=IN + 4 * MB)), ("gdn", dict(out=FAKE + 0x4000)),
+    ("gdn", dict(out=WS + 0x100)), ("gdn", dict(q=FAKE)), ("kda", dict(decay=WS + 0x1000)),
+    ("rwkv6", dict(beta=0, bonus=IN + 5 * MB + 0x10)),
 ])
 def test_decode_step_rejects_bad_args_without_state_change(op, over):
     cfg = dl.make_config(op, "bf16", 2, 4, 64, 64, 4)
-    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
     try:
         with pytest.raises(dl.DeltaLogError) as ei:
             dl.dl_decode_step(h, _args(**over))
@@ -156,10 +171,41 @@ def test_decode_step_rejects_bad_args_without_state_change(op, over):
     assert lib.dl_decode_step(None, ctypes.byref(_args()), None) == B.DL_ERR_ARG
 
 
+def test_eager_state_must_not_alias_the_token():
+    cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 1)
+    for over in (dict(out=FAKE + 0x1000), dict(q=FAKE), dict(v=FAKE + 0x800)):
+        with pytest.raises(dl.DeltaLogError) as ei:
+            dl.dl_eager_step(cfg, FAKE, _args(**over))
+        assert ei.value.status == B.DL_ERR_ARG
+        assert "state" in dl.dl_last_error()
+
+
+def test_materialize_dst_must_not_overlap_what_the_handle_holds():
+    cfg = dl.make_config("kda", "bf16", 2, 4, 64, 64, 4)
+    lib = B.load_library()
+    state_bytes = 8 * 64 * 64 * 4
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
+    try:
+        assert lib.dl_set_split_replay(h, PREP, dl.dl_prep_bytes(cfg)) == B.DL_OK
+        # partial overlaps with the base (from either side), the workspace, the prep records
+        for dst in (FAKE + 0x100, FAKE - state_bytes + 0x100, WS - 0x1000, WS + 0x2000, PREP - 0x100):
+            assert lib.dl_materialize(h, dst, None) == B.DL_ERR_ARG, hex(dst)
+            assert "dst overlaps" in dl.dl_last_error()
+        blk = 4 * 64 * 64 * 4
+        for dst in (FAKE + 0x100, WS, PREP + 0x100):
+            assert lib.dl_materialize_slot(h, 1, dst, None) == B.DL_ERR_ARG, hex(dst)
+        # prep over the base or the workspace is refused too
+        assert lib.dl_set_split_replay(h, FAKE + 0x400, dl.dl_prep_bytes(cfg)) == B.DL_ERR_ARG
+        assert lib.dl_set_split_replay(h, WS + 0x400, dl.dl_prep_bytes(cfg)) == B.DL_ERR_ARG
+        assert blk  # the slot's block is part of the base
+    finally:
+        dl.dl_state_destroy(h)
+
+
 def test_decode_tokens_validates_before_launching():
     cfg = dl.make_config("kda", "bf16", 2, 4, 64, 64, 4)
     lib = B.load_library()
-    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
     try:
         for K in (0, 9):
             arr = (B.StepArgs * max(K, 1))(*([_args()] * max(K, 1)))
@@ -171,11 +217,28 @@ def test_decode_tokens_validates_before_launching():
         assert dl.dl_log_length(h) == 0
     finally:
         dl.dl_state_destroy(h)
+    # tokens of one call: no output over another token's input or output
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
+    try:
+        t0 = _args()
+        t1 = _args(q=IN + 8 * MB, k=IN + 9 * MB, v=IN + 10 * MB, beta=IN + 11 * MB, decay=IN + 12 * MB,
+                   out=IN + 13 * MB)
+        for bad in (_args(**{**{f: getattr(t1, f) for f in ("q", "k", "v", "beta", "decay")}, "out": IN + 5 * MB}),
+                    _args(**{**{f: getattr(t1, f) for f in ("q", "k", "v", "beta", "decay")}, "out": IN + MB})):
+            with pytest.raises(dl.DeltaLogError) as ei:
+                dl.dl_decode_tokens(h, [t0, bad])
+            assert ei.value.status == B.DL_ERR_ARG
+            assert "another token" in dl.dl_last_error() or "overlapping outputs" in dl.dl_last_error()
+        assert dl.dl_log_length(h) == 0
+    finally:
+        dl.dl_state_destroy(h)
     # RWKV6: one bonus for all tokens of a call
     cfg = dl.make_config("rwkv6", "bf16", 2, 4, 64, 64, 4)
-    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
     try:
-        a0, a1 = _args(beta=0, bonus=FAKE + 0x600), _args(beta=0, bonus=FAKE + 0x700)
+        a0 = _args(beta=0, bonus=IN + 6 * MB)
+        a1 = _args(q=IN + 8 * MB, k=IN + 9 * MB, v=IN + 10 * MB, beta=0, decay=IN + 12 * MB, out=IN + 13 * MB,
+                   bonus=IN + 7 * MB)
         with pytest.raises(dl.DeltaLogError) as ei:
             dl.dl_decode_tokens(h, [a0, a1])
         assert ei.value.status == B.DL_ERR_ARG
@@ -188,7 +251,7 @@ def test_decode_tokens_validates_before_launching():
 def test_slot_calls_validate_on_the_host():
     cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)
     lib = B.load_library()
-    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
     try:
         # a lockstep handle has no slots
         with pytest.raises(dl.DeltaLogError):
@@ -209,9 +272,9 @@ def test_slot_calls_validate_on_the_host():
 def test_per_slot_fold_calls_validate_on_the_host():
     cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)
     lib = B.load_library()
-    dst = FAKE + 0x20000000
+    dst = DST
     assert lib.dl_materialize_slot(None, 0, dst, None) == B.DL_ERR_ARG
-    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
     try:
         for slot in (-1, 2):
             assert lib.dl_materialize_slot(h, slot, dst, None) == B.DL_ERR_ARG
@@ -238,12 +301,16 @@ def test_split_replay_and_graph_validate_on_the_host():
     cfg = dl.make_config("gdn", "bf16", 2, 4, 64, 64, 4)
     lib = B.load_library()
     need = dl.dl_prep_bytes(cfg)
-    assert lib.dl_set_split_replay(None, FAKE, need) == B.DL_ERR_ARG
-    h = dl.dl_state_init(cfg, FAKE, FAKE + 0x10000000, dl.dl_workspace_bytes(cfg))
+    assert lib.dl_set_split_replay(None, PREP, need) == B.DL_ERR_ARG
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
     try:
-        assert lib.dl_set_split_replay(h, FAKE + 8, need) == B.DL_ERR_ARG  # misaligned
-        assert lib.dl_set_split_replay(h, FAKE, need - 4) == B.DL_ERR_WORKSPACE
-        assert lib.dl_set_split_replay(h, FAKE, need) == B.DL_OK
+        assert lib.dl_set_split_replay(h, PREP + 8, need) == B.DL_ERR_ARG  # misaligned
+        assert lib.dl_set_split_replay(h, PREP, need - 4) == B.DL_ERR_WORKSPACE
+        assert lib.dl_set_split_replay(h, PREP, need) == B.DL_OK
+        # with the prep records set, a token whose output lands in them is refused
+        with pytest.raises(dl.DeltaLogError) as ei:
+            dl.dl_decode_step(h, _args(out=PREP + 0x100))
+        assert "prep" in dl.dl_last_error()
         assert lib.dl_set_split_replay(h, None, 0) == B.DL_OK  # back to the fused form
         g = ctypes.c_void_p()
         arr = (B.StepArgs * 4)(*([_args()] * 4))

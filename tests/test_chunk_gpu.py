@@ -66,15 +66,13 @@ def test_chunks_match_oracle(op, dtype, d, C, sizes):
         bounds.append(t)
     ref = gs.oracle_run(x, op, chk_steps=bounds)
     outs, states, st = run_chunks(dev, op, dtype, C, sizes, state_steps=set(bounds))
-    o = outs.cpu().numpy().reshape(T, Bsz * H, d)
-    eo = max(gs.rel(o[t], ref["out"][t]) for t in range(T))
-    es = max(gs.rel(states[b].numpy(), ref["states"][m]) for m, b in enumerate(bounds))
-    assert eo <= gs.OUT_GATE, eo
-    assert es <= gs.STATE_GATE, es
+    gs.assert_outputs(outs.cpu().numpy().reshape(T, Bsz * H, d), ref["out"])
+    for m, b in enumerate(bounds):
+        gs.assert_state(states[b].numpy(), ref["states"][m], b)
     assert st.log_length == T % C
     # and the single-token path agrees far inside the gates
     single, _, _ = gs.run_deltalog(dev, op, dtype, C)
-    assert max(gs.rel(outs[t].cpu(), single[t].cpu()) for t in range(T)) <= 1e-5
+    gs.assert_close_pair(outs, single, 1, 1e-5, "chunks vs single steps")
 
 
 FULL_CASES = [("gdn_b128_h32_d128", "gdn", (4,)), ("gdn_b128_h32_d128", "gdn", (8,)),
@@ -101,10 +99,9 @@ def test_full_size_chunks(name, op, sizes):
     ref = gs.oracle_run(x, op, heads=heads, chk_steps=chk, nthreads=16)
     outs, states, _ = run_chunks(dev, op, w.in_dtype, 8, sizes, state_steps=set(chk))
     hs = torch.as_tensor(heads, dtype=torch.long, device=outs.device)
-    o = outs.view(T, w.heads, w.d)[:, hs].cpu().numpy()
-    assert max(gs.rel(o[t], ref["out"][t]) for t in range(T)) <= gs.OUT_GATE
+    gs.assert_outputs(outs.view(T, w.heads, w.d)[:, hs].cpu().numpy(), ref["out"], sizes)
     for m, b in enumerate(chk):
-        assert gs.rel(states[b].numpy()[heads], ref["states"][m]) <= gs.STATE_GATE, b
+        gs.assert_state(states[b].numpy()[heads], ref["states"][m], (sizes, b))
 
 
 def test_token_axes_must_agree():

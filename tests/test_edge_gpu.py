@@ -32,10 +32,9 @@ def _check(x, op, dtype, C, T):
     ref = gs.oracle_run(x, op, chk_steps=steps)
     outs, states, _ = gs.run_deltalog(dev, op, dtype, C, state_steps=steps)
     Bsz, H, d = x["q"].shape[1], x["q"].shape[2], x["v"].shape[-1]
-    o = outs.cpu().numpy().reshape(T, Bsz * H, d)
-    eo = max(gs.rel(o[t], ref["out"][t]) for t in range(T))
-    es = max(gs.rel(states[t].numpy(), ref["states"][t]) for t in steps)
-    assert eo <= gs.OUT_GATE and es <= gs.STATE_GATE, (eo, es)
+    gs.assert_outputs(outs.cpu().numpy().reshape(T, Bsz * H, d), ref["out"])
+    for t in steps:
+        gs.assert_state(states[t].numpy(), ref["states"][t], t)
     return outs, states
 
 
@@ -83,6 +82,7 @@ def test_exact_overwrite_on_basis_keys(op):
         rows = S[torch.arange(Bsz * H), idx[t - 1].reshape(-1)]
         ref = x["v"][t - 1].reshape(Bsz * H, d)
         assert gs.rel(rows.numpy(), ref.numpy()) <= 1e-5, t
+        assert gs.head_err(rows.numpy(), ref.numpy(), 1) <= gs.ELEM_OUT_GATE, t
 
 
 @pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])

@@ -51,12 +51,10 @@ def test_split_every_step(op, dtype, d, C):
     ref = gs.oracle_run(x, op, chk_steps=steps)
     outs, states, st = gs.run_deltalog(dev, op, dtype, C, state_steps=steps, split_replay=True)
     fused, _, _ = gs.run_deltalog(dev, op, dtype, C)
-    o = outs.cpu().numpy().reshape(T, Bsz * H, d)
-    eo = max(gs.rel(o[t], ref["out"][t]) for t in range(T))
-    es = max(gs.rel(states[t].numpy(), ref["states"][m]) for m, t in enumerate(steps))
-    assert eo <= gs.OUT_GATE and es <= gs.STATE_GATE, (eo, es)
-    ef = max(gs.rel(outs[t].cpu(), fused[t].cpu()) for t in range(T))
-    assert ef <= 1e-6, ef
+    gs.assert_outputs(outs.cpu().numpy().reshape(T, Bsz * H, d), ref["out"])
+    for m, t in enumerate(steps):
+        gs.assert_state(states[t].numpy(), ref["states"][m], t)
+    gs.assert_close_pair(outs, fused, 1, 1e-6, "split vs fused")
     assert st.log_length == T % C
 
 
@@ -76,7 +74,7 @@ def test_split_log_equals_fused(op):
     (xf, kf, gf), (xs, ks, gs_) = logs
     assert torch.equal(kf, ks)
     assert torch.equal(gf, gs_)
-    assert gs.rel(xs, xf) <= 1e-6
+    gs.assert_close_pair(xs, xf, 1, 1e-6, "value factors")
 
 
 @pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
@@ -94,8 +92,7 @@ def test_switching_mid_cycle(op):
             st.set_split_replay(st.prep is None or t % 2 == 0)
 
     mixed, _, _ = gs.run_deltalog(dev, op, "bf16", C, on_step=flip)
-    ef = max(gs.rel(mixed[t].cpu(), fused[t].cpu()) for t in range(T))
-    assert ef <= 1e-6, ef
+    gs.assert_close_pair(mixed, fused, 1, 1e-6, "switching vs fused")
 
 
 def _static_tokens(dev, C, Bsz, H, d):
@@ -143,7 +140,7 @@ def test_graph_replay_equals_direct(op, split):
         assert st.log_length == 0
     assert torch.equal(base, dst.base)
     ref = gs.oracle_run(x, op, chk_steps=[T])
-    assert gs.rel(base.cpu().numpy().reshape(Bsz * H, d, d), ref["states"][0]) <= gs.STATE_GATE
+    gs.assert_state(base.cpu().numpy().reshape(Bsz * H, d, d), ref["states"][0])
     graph.close()
 
 
@@ -193,12 +190,10 @@ def test_full_size_split_against_oracle(name):
     outs, states, _ = gs.run_deltalog(dev, w.op, w.in_dtype, C, state_steps=steps, heads=heads,
                                       split_replay=True)
     hs = torch.as_tensor(heads, dtype=torch.long, device=outs.device)
-    o = outs.view(T, N, w.d)[:, hs].cpu().numpy()
-    eo = max(gs.rel(o[t], ref["out"][t]) for t in range(T))
-    es = max(gs.rel(states[t].numpy(), ref["states"][m]) for m, t in enumerate(steps))
-    _log(f"  max out rel {eo:.3e}, max state rel {es:.3e}")
-    assert eo <= gs.OUT_GATE and es <= gs.STATE_GATE
+    eo, eo_el = gs.assert_outputs(outs.view(T, N, w.d)[:, hs].cpu().numpy(), ref["out"])
+    for m, t in enumerate(steps):
+        gs.assert_state(states[t].numpy(), ref["states"][m], t)
+    _log(f"  out rel {eo:.3e} / per head {eo_el:.3e}")
     fused, _, _ = gs.run_deltalog(dev, w.op, w.in_dtype, C)
-    ef = max(gs.rel(outs[t].cpu(), fused[t].cpu()) for t in range(T))
-    _log(f"  split vs fused (all heads) max rel {ef:.3e}")
-    assert ef <= 1e-6
+    ef = gs.assert_close_pair(outs, fused, 1, 1e-6, "split vs fused")
+    _log(f"  split vs fused (all heads) rel / per head {ef}")

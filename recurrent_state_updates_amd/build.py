@@ -19,8 +19,13 @@ LIB = os.path.join(PKG, "libdeltalog.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["deltalog.cpp", "kernels_gdn.hip", "kernels_kda.hip", "kernels_rwkv6.hip", "slots.hip",
-           "kernels_gdn_chunk.hip", "kernels_kda_chunk.hip", "kernels_rwkv6_chunk.hip"]
+# (source, object name, extra defines): the kernel instantiation units are
+# compiled once per (operator, key width), so that they build in parallel.
+OPS = {0: "gdn", 1: "kda", 2: "rwkv6"}
+KEY_WIDTHS = (32, 64, 128)
+SOURCES = [("deltalog.cpp", "deltalog", []), ("slots.hip", "slots", []), ("probe.hip", "probe", [])] + [
+    (f"kernels_{kind}.hip", f"kernels_{kind}_{OPS[op]}_dk{dk}", [f"-DDLK_OP={op}", f"-DDLK_DK={dk}"])
+    for kind in ("step", "chunk") for op in OPS for dk in KEY_WIDTHS]
 
 # Packed fp32 VALU ops are switched off for all device code; the host pass
 # prints that it does not know the feature, which is harmless.  Matrix-core
@@ -92,9 +97,18 @@ def check_resources(src, lines):
     return blocks
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def _default_jobs():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 4
+    return max(1, min(16, n))
+
+
+def build(verbose: bool = False, jobs: int = None) -> str:
     """Compile and link the library; returns its path."""
     hipcc = _hipcc()
+    jobs = jobs or _default_jobs()
     os.makedirs(BUILD_DIR, exist_ok=True)
     # a refused or failed build leaves no library behind to be loaded
     tmp = LIB + ".tmp"
@@ -102,16 +116,18 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         if os.path.exists(path):
             os.remove(path)
     objs, cmds = [], []
-    for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    for src, name, defines in SOURCES:
+        obj = os.path.join(BUILD_DIR, name + ".o")
         objs.append(obj)
         extra = RESOURCE_REMARKS if src.endswith(".hip") else []
-        cmds.append((src, [hipcc, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]))
+        cmds.append((name, src, [hipcc, *FLAGS, *defines, *extra, "-c", os.path.join(CSRC, src), "-o", obj]))
+    # the longest units first, so that they do not start last
+    order = sorted(cmds, key=lambda c: (not c[0].startswith("kernels_chunk"), not c[0].endswith("dk128")))
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        outs = list(ex.map(lambda sc: (sc[0], _run(sc[1], verbose)), cmds))
-    for src, lines in outs:
+        outs = list(ex.map(lambda c: (c[0], c[1], _run(c[2], verbose)), order))
+    for name, src, lines in outs:
         if src.endswith(".hip"):
-            check_resources(src, lines)
+            check_resources(name, lines)
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB

@@ -61,10 +61,11 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
 }
 
 // MM selects the matrix-core form of the token products (phase C) and of the
-// fold, at D = 128.  A workgroup holds a whole head: waves 2h and 2h + 1 hold
-// column half h, rows 0-63 and 64-127, 16 lanes per (row, half), so that each
-// 16x16x4 k-step is four rows of one half and two waves' products add up per
-// column.  The vector form (D = 32, 64) holds whole heads as row passes.
+// fold, at DK = DV = 128.  A workgroup holds a whole head: waves 2h and 2h + 1
+// hold column half h, rows 0-63 and 64-127, 16 lanes per (row, half), so that
+// each 16x16x4 k-step is four rows of one half and two waves' products add up
+// per column.  The vector form (every other shape) holds whole heads as row
+// passes.
 // SEG runs every segment of the call in one workgroup: when the log fills
 // before the call's last token, the fold updates the register tile in place
 // and the rest of the tokens start an empty log from it (per-slot handles,
@@ -72,10 +73,10 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
 // segmented matrix-core form at C <= 8 asks for three waves per SIMD, which
 // the compiler meets without spilling (left alone, KDA settles one register
 // above that, at two waves).
-template <int OP, typename TIn, int D, int TV, int NT, int CMAX, bool MM, bool SEG>
+template <int OP, typename TIn, int DK, int DV, int TV, int NT, int CMAX, bool MM, bool SEG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SEG && MM && CMAX == 8 ? 3 : 1)))
 void chunk_kernel(const ChunkParams p) {
-    using G = Geom<D, TV, NT>;
+    using G = Geom<DK, DV, TV, NT>;
     constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
     constexpr int KL = G::KL, EPP = G::EPP;
     constexpr bool GDN = OP == OP_GDN;
@@ -83,14 +84,14 @@ void chunk_kernel(const ChunkParams p) {
     constexpr int KM = KMAX_TOKENS;
     constexpr int CP = CMAX;  // entry slots: old entries plus the chunk's tokens (<= C <= CMAX)
     constexpr int KPASS = (CMAX + EPP - 1) / EPP;
-    static_assert(!MM || (D == 128 && TV == D && NT == 256 && 2 * KM == 16),
-                  "matrix-core form: whole heads at D = 128, 256 threads, 16 product vectors");
+    static_assert(!MM || (DK == 128 && DV == 128 && TV == DV && NT == 256 && 2 * KM == 16),
+                  "matrix-core form: whole 128 x 128 heads, 256 threads, 16 product vectors");
     // s[i] holds tile row rbase + RSTEP * i; xrow[j] holds log entry ebase + ESTEP * j
     constexpr int RSTEP = MM ? 4 : RPP;
     constexpr int ESTEP = MM ? 8 : RPP;
     constexpr int NWR = MM ? 2 : NW;  // row blocks whose products add up in each column
     constexpr int XR = (CMAX + ESTEP - 1) / ESTEP;
-    constexpr int GW = GDN ? 1 : D;  // log-decay values per entry
+    constexpr int GW = GDN ? 1 : DK;  // log-decay values per entry
     using TX = typename std::conditional<DELTA, float, TIn>::type;
     using Raw = typename In4<TIn>::raw;
     using RawX = typename In4<TX>::raw;
@@ -107,7 +108,7 @@ void chunk_kernel(const ChunkParams p) {
     // RWKV6 has no key-side products: no scaled keys, and one side of products
     constexpr int NS = DELTA ? 2 : 1;          // sides of products: keys (delta rules), queries
     constexpr int ZS = NS - 1;                 // index of the query side
-    constexpr int SZ_K = KM * D;               // floats; every size a multiple of 4
+    constexpr int SZ_K = KM * DK;              // floats; every size a multiple of 4
     constexpr int SZ_MV0 = DELTA ? SZ_K : 0;
     constexpr int SZ_LG = (KM * GW + 3) & ~3;
     constexpr int SZ_G = ((KM + 1) * GW + 3) & ~3;
@@ -115,18 +116,18 @@ void chunk_kernel(const ChunkParams p) {
     constexpr int SZ_RED = KM * NWR * NS * TV;
     constexpr int POOL = MM ? (SZ_B > SZ_RED ? SZ_B : SZ_RED) : SZ_B + SZ_RED;
     __shared__ __attribute__((aligned(16))) float s_pool[POOL];
-    auto &s_k = *reinterpret_cast<float (*)[KM][D]>(s_pool);                   // token keys
-    auto &s_q = *reinterpret_cast<float (*)[KM][D]>(s_pool + SZ_K);            // token queries (receptances)
+    auto &s_k = *reinterpret_cast<float (*)[KM][DK]>(s_pool);                   // token keys
+    auto &s_q = *reinterpret_cast<float (*)[KM][DK]>(s_pool + SZ_K);            // token queries (receptances)
     // 2^{rho_t} k_t and 2^{rho_t} q_t (r_t), row r stored at mv_at(r) so that the R
     // rows of one thread (rbase, rbase + RSTEP, ...) are contiguous
     // (s_mv0 is empty for RWKV6 and never read or written there)
-    auto &s_mv1 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 2 * SZ_K);
-    auto &s_mv0 = *reinterpret_cast<float (*)[KM][D]>(s_pool + 3 * SZ_K);
+    auto &s_mv1 = *reinterpret_cast<float (*)[KM][DK]>(s_pool + 2 * SZ_K);
+    auto &s_mv0 = *reinterpret_cast<float (*)[KM][DK]>(s_pool + 3 * SZ_K);
     auto &s_lg = *reinterpret_cast<float (*)[KM][GW]>(s_pool + 3 * SZ_K + SZ_MV0);  // log2 of each token's decay
     auto &s_g = *reinterpret_cast<float (*)[KM + 1][GW]>(s_pool + 3 * SZ_K + SZ_MV0 + SZ_LG);  // g_{t-1} at index t (g_{-1} = g_L)
     auto &s_red = *reinterpret_cast<float (*)[KM][NWR][NS][TV]>(s_pool + (MM ? 0 : SZ_B));
-    __shared__ __attribute__((aligned(16))) float s_scale[D];      // fold: 2^{g_{K-1}} per row
-    __shared__ __attribute__((aligned(16))) float s_kt[CP * D];    // fold: decayed keys [entry][row]
+    __shared__ __attribute__((aligned(16))) float s_scale[DK];     // fold: 2^{g_{K-1}} per row
+    __shared__ __attribute__((aligned(16))) float s_kt[CP * DK];   // fold: decayed keys [entry][row]
     // value factors [entry][col] for the fold.  In the matrix-core form rows
     // L .. L+K-1 first hold the chunk's values (phase D reads v_t there and
     // writes u_t in its place), and row CP takes the writes of token slots past
@@ -164,7 +165,7 @@ void chunk_kernel(const ChunkParams p) {
     const int cq = MM ? 64 * (wave >> 1) + 4 * (lane & 15) : 4 * (tid % LPR);
     const int ebase = MM ? 4 * (wave & 1) + (lane >> 4) : tid / LPR;
     const int rblk = MM ? (wave & 1) : wave;
-    auto mv_at = [](int row) { return (row % RSTEP) * (D / RSTEP) + row / RSTEP; };
+    auto mv_at = [](int row) { return (row % RSTEP) * (DK / RSTEP) + row / RSTEP; };
     const int col0 = tile * TV;
     const int c4 = 4 * (tid % KL);
     const int ke = tid / KL;            // key-side group: token ke, then entries ps*EPP + ke
@@ -184,25 +185,25 @@ void chunk_kernel(const ChunkParams p) {
     // this thread's column (slots past the segment re-read its first token,
     // a valid address, and are never used)
     auto load_tokens = [&]() {
-        kraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.k, tb, t0, K, g) + (size_t)n * D + c4);
-        qraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.q, tb, t0, K, g) + (size_t)n * D + c4);
+        kraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.k, tb, t0, K, g) + (size_t)n * DK + c4);
+        qraw = *reinterpret_cast<global_ptr<Raw>>(group_pick<TIn, GPW>(p.q, tb, t0, K, g) + (size_t)n * DK + c4);
         const global_ptr<float> dec_t = group_pick<float, GPW>(p.decay, tb, t0, K, g);
         if (GDN)
             alpha = dec_t[n];
         else
-            dec4 = *reinterpret_cast<global_ptr<f4>>(dec_t + (size_t)n * D + c4);
+            dec4 = *reinterpret_cast<global_ptr<f4>>(dec_t + (size_t)n * DK + c4);
         if (DELTA) beta_t = group_pick<float, GPW>(p.beta, tb, t0, K, g)[n];
         const void *v0 = opaque_scalar(p.v[tb]);
 #pragma unroll
         for (int t = 0; t < KM; ++t) {
             const void *vt = t == 0 ? v0 : opaque_scalar(p.v[min(tb + t, KM - 1)]);
             vt = t < K ? vt : v0;
-            vraw[t] = ((global_ptr<TIn>)static_cast<const TIn *>(vt))[(size_t)n * D + col0 + tid % TV];
+            vraw[t] = ((global_ptr<TIn>)static_cast<const TIn *>(vt))[(size_t)n * DV + col0 + tid % TV];
         }
     };
     load_tokens();
     f4 bon4 = {0.f, 0.f, 0.f, 0.f};
-    if (!DELTA) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
+    if (!DELTA) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * DK + c4);
     float glast_s = 0.f;
     f4 glast4 = {0.f, 0.f, 0.f, 0.f};
     Raw klog[KPASS];
@@ -214,30 +215,30 @@ void chunk_kernel(const ChunkParams p) {
         if (GDN)
             glast_s = p.logG[el];
         else
-            glast4 = *reinterpret_cast<const f4 *>(p.logG + el * D + c4);
+            glast4 = *reinterpret_cast<const f4 *>(p.logG + el * DK + c4);
 #pragma unroll
         for (int ps = 0; ps < KPASS; ++ps) {
             const size_t e = (size_t)n * C + min(ps * EPP + ke, last);
-            klog[ps] = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.logK) + e * D + c4);
+            klog[ps] = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.logK) + e * DK + c4);
             if (GDN)
                 glog_s[ps] = p.logG[e];
             else
-                glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * D + c4);
+                glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * DK + c4);
         }
-        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0 + cq;
+        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * DV + col0 + cq;
 #pragma unroll
         for (int j = 0; j < XR; ++j)
-            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(ebase + ESTEP * j, last) * D);
+            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(ebase + ESTEP * j, last) * DV);
     }
     // the small loads above all go out before the tile's (loads complete in
     // issue order, so one placed after the tile could only be used once the
     // whole tile has arrived; the matrix-core form uses the values early)
     if constexpr (MM) __builtin_amdgcn_sched_barrier(0);
-    const size_t tile4 = (size_t)n * (D * D / 4) + (col0 + cq) / 4 + (size_t)rbase * (D / 4);
+    const size_t tile4 = (size_t)n * (DK * DV / 4) + (col0 + cq) / 4 + (size_t)rbase * (DV / 4);
     const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
     f4 s[R];
 #pragma unroll
-    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RSTEP * (D / 4));
+    for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RSTEP * (DV / 4));
     // every load above is issued before anything consumes one (a consumer
     // scheduled among them would wait for all loads issued before it)
     __builtin_amdgcn_sched_barrier(0);
@@ -332,11 +333,11 @@ void chunk_kernel(const ChunkParams p) {
             }
             if (!fold && tile == 0) {  // entry L + t of the log: the key copy and its log-decay
                 const size_t e = (size_t)n * C + L + t;
-                *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * D + c4) = kraw;
+                *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * DK + c4) = kraw;
                 if (GDN) {
                     if (c4 == 0) p.logG[e] = g_at(t + 1).x;
                 } else {
-                    *reinterpret_cast<f4 *>(p.logG + e * D + c4) = g_at(t + 1);
+                    *reinterpret_cast<f4 *>(p.logG + e * DK + c4) = g_at(t + 1);
                 }
             }
         }
@@ -395,7 +396,7 @@ void chunk_kernel(const ChunkParams p) {
                 }
             }
             if (fold && (is_old || is_new))
-                *reinterpret_cast<f4 *>(&s_kt[e * D + c4]) = ke4 * exp2v(gend - ge4);
+                *reinterpret_cast<f4 *>(&s_kt[e * DK + c4]) = ke4 * exp2v(gend - ge4);
         }
         if (fold) {
             // old value factors of the tile for the fold; zero the slots up to a multiple of four
@@ -404,11 +405,12 @@ void chunk_kernel(const ChunkParams p) {
                 const int i = ebase + ESTEP * j;
                 if (FIRST && i < L) *reinterpret_cast<f4 *>(&s_x[i * TV + cq]) = In4<TX>::unpack(xrow[j]);
             }
+            constexpr int W = DK > TV ? DK : TV;
             const int pad = ((NE + 3) & ~3) - NE;
-            for (int idx = tid; idx < pad * D; idx += NT) {
-                const int i = NE + idx / D;
-                const int c = idx % D;
-                s_kt[i * D + c] = 0.f;
+            for (int idx = tid; idx < pad * W; idx += NT) {
+                const int i = NE + idx / W;
+                const int c = idx % W;
+                if (c < DK) s_kt[i * DK + c] = 0.f;
                 if (c < TV) s_x[i * TV + c] = 0.f;
             }
         }
@@ -535,15 +537,15 @@ void chunk_kernel(const ChunkParams p) {
                     o = zj + s_dot[t] * vj;
                 }
                 xs[t] = xnew;
-                p.out[tb + t][(size_t)n * D + j] = o;
+                p.out[tb + t][(size_t)n * DV + j] = o;
                 if (fold) {
                     s_x[(L + t) * TV + jt] = xnew;
                 } else {
                     const size_t e = (size_t)n * C + L + t;
                     if (DELTA)
-                        static_cast<float *>(p.logX)[e * D + j] = xnew;
+                        static_cast<float *>(p.logX)[e * DV + j] = xnew;
                     else
-                        store_raw(static_cast<TIn *>(p.logX) + e * D + j, vj);
+                        store_raw(static_cast<TIn *>(p.logX) + e * DV + j, vj);
                 }
             }
         }
@@ -570,7 +572,7 @@ void chunk_kernel(const ChunkParams p) {
 #pragma unroll
                     for (int c = 0; c < 4; ++c) pc[c] = m4{0.f, 0.f, 0.f, 0.f};
                     for (int e = 0; e < NE; e += 4) {
-                        const float av = s_kt[(e + kr) * D + arow];
+                        const float av = s_kt[(e + kr) * DK + arow];
                         const f4 bv = *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + cq]);
 #pragma unroll
                         for (int c = 0; c < 4; ++c) pc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[c], pc[c], 0, 0, 0);
@@ -579,7 +581,7 @@ void chunk_kernel(const ChunkParams p) {
                     for (int q = 0; q < 4; ++q) {
                         const int i = 4 * g + q;
                         const f4 o = s[i] * s_scale[rbase + RSTEP * i] + f4{pc[0][q], pc[1][q], pc[2][q], pc[3][q]};
-                        __builtin_nontemporal_store(o, dst4 + (size_t)i * RSTEP * (D / 4));
+                        __builtin_nontemporal_store(o, dst4 + (size_t)i * RSTEP * (DV / 4));
                         if constexpr (SEG) s[i] = o;
                     }
                 }
@@ -595,12 +597,12 @@ void chunk_kernel(const ChunkParams p) {
 #pragma unroll
                     for (int i = 0; i < R; ++i) {
                         const int row = rbase + RSTEP * i;
-                        acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
-                                  s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
+                        acc[i] += s_kt[(e + 0) * DK + row] * x0 + s_kt[(e + 1) * DK + row] * x1 +
+                                  s_kt[(e + 2) * DK + row] * x2 + s_kt[(e + 3) * DK + row] * x3;
                     }
                 }
 #pragma unroll
-                for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RSTEP * (D / 4));
+                for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RSTEP * (DV / 4));
                 if constexpr (SEG) {
 #pragma unroll
                     for (int i = 0; i < R; ++i) s[i] = acc[i];
@@ -628,54 +630,61 @@ void chunk_kernel(const ChunkParams p) {
     }
 }
 
-// Tile shape of the chunk kernel: one workgroup per head -- 64 KB over 256
-// threads of sixteen float4 at D = 128 (the matrix-core form), 16 KB over 128
-// threads at D = 64 and 4 KB over 64 threads at D = 32 (the vector form).
-template <int D>
+// Tile shape of the chunk kernel: one workgroup per head.  At 128 x 128 the
+// matrix-core form: 64 KB over 256 threads of sixteen float4.  Elsewhere the
+// vector form, eight float4 per thread where the head allows it (four at 32
+// x 32, 64 x 32 and 128 x 32), with at least one key-side group of lanes per
+// token (2 DK threads) and one thread per value column: 16 KB over 128
+// threads at 64 x 64, 4 KB over 64 at 32 x 32.
+template <int DK, int DV>
 struct ChunkShape {
-    static constexpr int TV = D;
-    static constexpr int NT = D == 128 ? 256 : (D == 64 ? 128 : 64);
+    static constexpr bool MM = DK == 128 && DV == 128;
+    static constexpr int TV = DV;
+    static constexpr int A = 2 * DK > DV ? 2 * DK : DV;
+    static constexpr int B = DK * DV / 32 > 64 ? DK * DV / 32 : 64;
+    static constexpr int NT = MM ? 256 : (A > B ? A : B);
 };
 
-// The matrix cores form the token products at D = 128 (measured: whole heads
-// there run faster on them than on the vector ALUs from two tokens on; the
-// library sends a single token to the single-token kernel).  The 16 KB heads
-// of D = 64 and below stay on the vector ALUs.
-template <int OP, typename TIn, int D, int CMAX, bool SEG>
+// The matrix cores form the token products at 128 x 128 (measured: whole
+// heads there run faster on them than on the vector ALUs from two tokens on;
+// the library sends a single token to the single-token kernel).  The smaller
+// heads stay on the vector ALUs.
+template <int OP, typename TIn, int DK, int DV, int CMAX, bool SEG>
 hipError_t launch_chunk_form(const ChunkParams &p, hipStream_t s) {
-    constexpr int TV = ChunkShape<D>::TV, NT = ChunkShape<D>::NT;
+    using S = ChunkShape<DK, DV>;
     const unsigned blocks = (unsigned)p.N;
-    hipLaunchKernelGGL((chunk_kernel<OP, TIn, D, TV, NT, CMAX, D == 128, SEG>), dim3(blocks), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((chunk_kernel<OP, TIn, DK, DV, S::TV, S::NT, CMAX, S::MM, SEG>), dim3(blocks), dim3(S::NT),
+                       0, s, p);
     return hipGetLastError();
 }
 
-template <int OP, typename TIn, int D, int CMAX>
+template <int OP, typename TIn, int DK, int DV, int CMAX>
 hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
-    return p.segmented ? launch_chunk_form<OP, TIn, D, CMAX, true>(p, s)
-                       : launch_chunk_form<OP, TIn, D, CMAX, false>(p, s);
+    return p.segmented ? launch_chunk_form<OP, TIn, DK, DV, CMAX, true>(p, s)
+                       : launch_chunk_form<OP, TIn, DK, DV, CMAX, false>(p, s);
 }
 
-template <int OP, typename TIn, int D>
+template <int OP, typename TIn, int DK, int DV>
 hipError_t launch_chunk_bounded(int cmax, const ChunkParams &p, hipStream_t s) {
-    if (cmax <= 8) return launch_chunk_one<OP, TIn, D, 8>(p, s);
-    if (cmax <= 16) return launch_chunk_one<OP, TIn, D, 16>(p, s);
-    return launch_chunk_one<OP, TIn, D, 32>(p, s);
+    if (cmax <= 8) return launch_chunk_one<OP, TIn, DK, DV, 8>(p, s);
+    if (cmax <= 16) return launch_chunk_one<OP, TIn, DK, DV, 16>(p, s);
+    return launch_chunk_one<OP, TIn, DK, DV, 32>(p, s);
 }
 
-template <int OP, typename TIn>
-hipError_t launch_chunk_width(int D, int cmax, const ChunkParams &p, hipStream_t s) {
-    switch (D) {
-        case 32: return launch_chunk_bounded<OP, TIn, 32>(cmax, p, s);
-        case 64: return launch_chunk_bounded<OP, TIn, 64>(cmax, p, s);
-        case 128: return launch_chunk_bounded<OP, TIn, 128>(cmax, p, s);
+template <int OP, typename TIn, int DK>
+hipError_t launch_chunk_value_width(int DV, int cmax, const ChunkParams &p, hipStream_t s) {
+    switch (DV) {
+        case 32: return launch_chunk_bounded<OP, TIn, DK, 32>(cmax, p, s);
+        case 64: return launch_chunk_bounded<OP, TIn, DK, 64>(cmax, p, s);
+        case 128: return launch_chunk_bounded<OP, TIn, DK, 128>(cmax, p, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <int OP>
-hipError_t launch_chunk_op(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s) {
-    return in_bf16 ? launch_chunk_width<OP, bf16_bits>(D, cmax, p, s)
-                   : launch_chunk_width<OP, float>(D, cmax, p, s);
+template <int OP, int DK>
+hipError_t launch_chunk(int in_bf16, int DV, int cmax, const ChunkParams &p, hipStream_t s) {
+    return in_bf16 ? launch_chunk_value_width<OP, bf16_bits, DK>(DV, cmax, p, s)
+                   : launch_chunk_value_width<OP, float, DK>(DV, cmax, p, s);
 }
 
 }  // namespace dlk

@@ -97,9 +97,8 @@ dl_status check_config(const dl_config *cfg, size_t *heads) {
     if (cfg->B <= 0 || cfg->H <= 0 || cfg->dk <= 0 || cfg->dv <= 0)
         return fail(DL_ERR_SHAPE, "B, H, dk and dv must be positive");
     if (cfg->C < 1 || cfg->C > DL_MAX_CAPACITY) return fail(DL_ERR_SHAPE, "C must lie in [1, 32]");
-    if (cfg->dk != cfg->dv) return fail(DL_ERR_UNSUPPORTED, "only dk == dv is built");
-    if (cfg->dk != 32 && cfg->dk != 64 && cfg->dk != 128)
-        return fail(DL_ERR_UNSUPPORTED, "dk must be 32, 64 or 128");
+    auto built = [](int w) { return w == 32 || w == 64 || w == 128; };
+    if (!built(cfg->dk) || !built(cfg->dv)) return fail(DL_ERR_UNSUPPORTED, "dk and dv must each be 32, 64 or 128");
     const size_t n = (size_t)cfg->B * (size_t)cfg->H;
     // a launch holds at most 2^32 work-items and the widest kernel runs 512 per head
     if (n > (size_t)DL_MAX_HEADS) return fail(DL_ERR_SHAPE, "B * H exceeds DL_MAX_HEADS");
@@ -206,15 +205,36 @@ dl_status check_step(const dl_state *h, const dl_step_args *a) {
     return check_token_aliasing(&h->cfg, a, w, nw);
 }
 
+// The single-token and multi-token kernels of one operator, by key width.
+template <int OP>
+hipError_t step_of_op(const dl_config *cfg, int mode, const dlk::StepParams &p, hipStream_t s) {
+    const int bf16 = cfg->in_dtype == DL_BF16, cmax = cmax_of(cfg);
+    switch (cfg->dk) {
+        case 32: return dlk::launch_step<OP, 32>(bf16, cfg->dv, mode, cmax, p, s);
+        case 64: return dlk::launch_step<OP, 64>(bf16, cfg->dv, mode, cmax, p, s);
+        case 128: return dlk::launch_step<OP, 128>(bf16, cfg->dv, mode, cmax, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int OP>
+hipError_t chunk_of_op(const dl_config *cfg, const dlk::ChunkParams &p, hipStream_t s) {
+    const int bf16 = cfg->in_dtype == DL_BF16, cmax = cmax_of(cfg);
+    switch (cfg->dk) {
+        case 32: return dlk::launch_chunk<OP, 32>(bf16, cfg->dv, cmax, p, s);
+        case 64: return dlk::launch_chunk<OP, 64>(bf16, cfg->dv, cmax, p, s);
+        case 128: return dlk::launch_chunk<OP, 128>(bf16, cfg->dv, cmax, p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 dl_status launch(const dl_config *cfg, int mode, const dlk::StepParams &p, void *stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int cmax = cmax_of(cfg);
-    const int bf16 = cfg->in_dtype == DL_BF16;
     hipError_t e;
     switch (cfg->op) {
-        case DL_GDN: e = dlk::launch_gdn(bf16, cfg->dk, mode, cmax, p, s); break;
-        case DL_KDA: e = dlk::launch_kda(bf16, cfg->dk, mode, cmax, p, s); break;
-        default: e = dlk::launch_rwkv6(bf16, cfg->dk, mode, cmax, p, s); break;
+        case DL_GDN: e = step_of_op<dlk::OP_GDN>(cfg, mode, p, s); break;
+        case DL_KDA: e = step_of_op<dlk::OP_KDA>(cfg, mode, p, s); break;
+        default: e = step_of_op<dlk::OP_RWKV6>(cfg, mode, p, s); break;
     }
     if (e != hipSuccess)
         return fail(DL_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
@@ -452,8 +472,6 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
         if (args[t].bonus != args[0].bonus)
             return fail(DL_ERR_ARG, "every token of a call must carry the same bonus");
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int cmax = cmax_of(&h->cfg);
-    const int bf16 = h->cfg.in_dtype == DL_BF16;
     // tokens t0 .. t0 + k - 1 of the call as one chunk
     auto chunk_of = [&](int t0, int k) {
         dlk::ChunkParams p = {};
@@ -480,9 +498,9 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     auto launch_chunk = [&](const dlk::ChunkParams &p) -> dl_status {
         hipError_t e;
         switch (h->cfg.op) {
-            case DL_GDN: e = dlk::launch_gdn_chunk(bf16, h->cfg.dk, cmax, p, s); break;
-            case DL_KDA: e = dlk::launch_kda_chunk(bf16, h->cfg.dk, cmax, p, s); break;
-            default: e = dlk::launch_rwkv6_chunk(bf16, h->cfg.dk, cmax, p, s); break;
+            case DL_GDN: e = chunk_of_op<dlk::OP_GDN>(&h->cfg, p, s); break;
+            case DL_KDA: e = chunk_of_op<dlk::OP_KDA>(&h->cfg, p, s); break;
+            default: e = chunk_of_op<dlk::OP_RWKV6>(&h->cfg, p, s); break;
         }
         if (e != hipSuccess)
             return fail(DL_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));

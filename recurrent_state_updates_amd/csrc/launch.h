@@ -22,24 +22,25 @@ enum { OP_GDN = 0, OP_KDA = 1, OP_RWKV6 = 2 };
 enum { MODE_APPEND = 0, MODE_MERGE = 1, MODE_EAGER = 2, MODE_FOLD = 3, MODE_AUTO = 4, MODE_PREP = 5,
        MODE_PREPPED = 6 };
 
-// Floats in one head's prep record for head width D and log bound cmax:
-// [0, D) scaled key, [D, 2D) scaled query (or receptance), then cmax key-side
-// and cmax query-side replay coefficients, then the token's scalar term.
-constexpr int prep_stride(int D, int cmax) { return 2 * D + 2 * cmax + 4; }
+// Floats in one head's prep record for key width DK and log bound cmax:
+// [0, DK) scaled key, [DK, 2DK) scaled query (or receptance), then cmax
+// key-side and cmax query-side replay coefficients, then the token's scalar
+// term.
+constexpr int prep_stride(int DK, int cmax) { return 2 * DK + 2 * cmax + 4; }
 
 struct StepParams {
-    float *base;         // [N][D][D] fp32 base (or dense state for EAGER)
+    float *base;         // [N][DK][DV] fp32 base (or dense state for EAGER)
     float *dst;          // state written by MERGE / EAGER / FOLD
-    const void *q;       // [N][D] input dtype: q (GDN, KDA) or r (RWKV6)
-    const void *k;       // [N][D] input dtype
-    const void *v;       // [N][D] input dtype
+    const void *q;       // [N][DK] input dtype: q (GDN, KDA) or r (RWKV6)
+    const void *k;       // [N][DK] input dtype
+    const void *v;       // [N][DV] input dtype
     const float *beta;   // [N]
-    const float *decay;  // [N] (GDN) or [N][D]
-    const float *bonus;  // [H][D] (RWKV6)
-    float *out;          // [N][D] fp32
-    void *logX;          // [N][C][D]: fp32 (GDN, KDA) or input dtype (RWKV6)
-    void *logK;          // [N][C][D] input dtype
-    float *logG;         // [N][C] (GDN) or [N][C][D] fp32, base-2 cumulative log-decay
+    const float *decay;  // [N] (GDN) or [N][DK]
+    const float *bonus;  // [H][DK] (RWKV6)
+    float *out;          // [N][DV] fp32
+    void *logX;          // [N][C][DV]: fp32 (GDN, KDA) or input dtype (RWKV6)
+    void *logK;          // [N][C][DK] input dtype
+    float *logG;         // [N][C] (GDN) or [N][C][DK] fp32, base-2 cumulative log-decay
     int L;               // log entries present before the launch
     int C;               // log capacity (entry stride of the log arrays)
     int H;               // heads per slot (bonus row = n % H)
@@ -50,26 +51,28 @@ struct StepParams {
     const int *slot_base;              // [B] decode-step index of the slot's last empty log
     const unsigned char *slot_active;  // [B] 1 = decode this slot
     unsigned step;                     // decode steps issued so far
-    float *prep;                       // [N][prep_stride(D, cmax)] split-replay records
+    float *prep;                       // [N][prep_stride(DK, cmax)] split-replay records
 };
 
-// Launch one mode for one operator.  in_bf16 selects the input dtype, D the
-// head width (dk == dv), cmax the compile-time bound on log entries (8, 16 or 32).
-hipError_t launch_gdn(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
-hipError_t launch_kda(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
-hipError_t launch_rwkv6(int in_bf16, int D, int mode, int cmax, const StepParams &p, hipStream_t s);
+// Launch one mode of the single-token kernel for operator OP and key width
+// DK (32, 64 or 128).  in_bf16 selects the input dtype, DV the value width
+// (32, 64 or 128), cmax the compile-time bound on log entries (8, 16 or 32).
+// Defined in step_launch.h; each (OP, DK) is instantiated in a translation
+// unit of its own (kernels_step.hip compiled with -DDLK_OP, -DDLK_DK).
+template <int OP, int DK>
+hipError_t launch_step(int in_bf16, int DV, int mode, int cmax, const StepParams &p, hipStream_t s);
 
 // Several consecutive tokens of every head in one launch (lockstep or per-slot logs).
 constexpr int KMAX_TOKENS = 8;
 struct ChunkParams {
-    float *base;                        // [N][D][D] fp32, rewritten in place when fold
-    const void *q[KMAX_TOKENS];         // token t: [N][D] input dtype
+    float *base;                        // [N][DK][DV] fp32, rewritten in place when fold
+    const void *q[KMAX_TOKENS];         // token t: [N][DK] input dtype (v: [N][DV])
     const void *k[KMAX_TOKENS];
     const void *v[KMAX_TOKENS];
     const float *beta[KMAX_TOKENS];     // [N] (GDN, KDA)
-    const float *decay[KMAX_TOKENS];    // [N] (GDN) or [N][D]
-    float *out[KMAX_TOKENS];            // [N][D] fp32
-    const float *bonus;                 // [H][D] (RWKV6)
+    const float *decay[KMAX_TOKENS];    // [N] (GDN) or [N][DK]
+    float *out[KMAX_TOKENS];            // [N][DV] fp32
+    const float *bonus;                 // [H][DK] (RWKV6)
     void *logX;
     void *logK;
     float *logG;
@@ -89,9 +92,10 @@ struct ChunkParams {
     unsigned step;
 };
 
-hipError_t launch_gdn_chunk(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s);
-hipError_t launch_kda_chunk(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s);
-hipError_t launch_rwkv6_chunk(int in_bf16, int D, int cmax, const ChunkParams &p, hipStream_t s);
+// The multi-token kernel for operator OP and key width DK; defined in
+// chunk_kernel.h, instantiated per (OP, DK) in kernels_chunk.hip.
+template <int OP, int DK>
+hipError_t launch_chunk(int in_bf16, int DV, int cmax, const ChunkParams &p, hipStream_t s);
 
 // Set slot_base / slot_active entries: slot < 0 means every slot (with
 // only_active, every active slot); set_base / set_active select the fields.

@@ -1,8 +1,8 @@
 // step_kernel.h -- the decode-step kernel family for gfx950.
 //
-// One workgroup owns a D x TV tile of one head's fp32 state: all D key rows
-// and TV of the D value columns (the pages' value-tile parallelism; the
-// single-token kernels use TV = D, one tile per head, see Shape).  Its
+// One workgroup owns a DK x TV tile of one head's fp32 state: all DK key rows
+// and TV of the DV value columns (the pages' value-tile parallelism; the
+// single-token kernels use TV = DV, one tile per head, see Shape).  Its
 // threads stream the tile once from HBM with coalesced 16-byte loads (a tile
 // row is TV/4 lanes wide), keep it in registers, and do everything else
 // around that single pass:
@@ -106,39 +106,47 @@ __device__ __forceinline__ f4 log2v(f4 a) {
     return o;
 }
 
-// Thread geometry of one workgroup over a D x TV tile (all D key rows, TV of
-// the D value columns) of one head's state.
-template <int D, int TV, int NT>
+// Thread geometry of one workgroup over a DK x TV tile (all DK key rows, TV
+// of the DV value columns) of one head's state.
+template <int DK, int DV, int TV, int NT>
 struct Geom {
-    static constexpr int NTILE = D / TV;  // value tiles per head
-    static constexpr int LPR = TV / 4;    // lanes per tile row (one float4 each)
-    static constexpr int RPP = NT / LPR;  // rows per pass of the workgroup
-    static constexpr int R = D / RPP;     // rows held by each thread
-    static constexpr int NW = NT / 64;    // waves
-    static constexpr int KL = D / 4;      // key-side lanes per log entry (4 channels each)
-    static constexpr int EPP = NT / KL;   // log entries per key-side pass
-    static_assert(D % TV == 0 && TV % 4 == 0 && NT % 64 == 0, "geometry");
-    static_assert(NT % LPR == 0 && D % RPP == 0 && R >= 1, "the tile must divide evenly");
+    static constexpr int NTILE = DV / TV;  // value tiles per head
+    static constexpr int LPR = TV / 4;     // lanes per tile row (one float4 each)
+    static constexpr int RPP = NT / LPR;   // rows per pass of the workgroup
+    static constexpr int R = DK / RPP;     // rows held by each thread
+    static constexpr int NW = NT / 64;     // waves
+    static constexpr int KL = DK / 4;      // key-side lanes per log entry (4 channels each)
+    static constexpr int EPP = NT / KL;    // log entries per key-side pass
+    static_assert(DV % TV == 0 && TV % 4 == 0 && NT % 64 == 0, "geometry");
+    static_assert(NT % LPR == 0 && DK % RPP == 0 && R >= 1, "the tile must divide evenly");
     static_assert(TV <= NT && KL <= 64 && NT % KL == 0, "column stage and key-side groups");
 };
 
 // Tile shape of the single-token kernels: one workgroup per head at every
-// width -- 64 KB at D = 128, 16 KB and 128 threads at D = 64, 4 KB and 64
-// threads at D = 32.  A whole head is one contiguous block, which streams
-// about 7 % faster on MI355X than two 64-column halves of it (rows read as
-// 256-byte pieces at a 512-byte stride), for the append and the fold alike.
-// At D = 128 the decode modes use 256 threads of sixteen float4 each: four
-// heads per CU instead of three, appends 2-4 % faster than with 512 threads
-// of eight.  The decode-and-fold keeps the append's shape, so that per-slot
-// decode (one kernel that appends or folds per slot) adds its column sums in
-// the same order as the lockstep kernels and gives the same bits.  The
+// width.  A thread holds eight float4 of the state (sixteen at 128 x 128),
+// with at least one thread per value column for the column stage and one
+// wave per workgroup: 64 KB over 256 threads at 128 x 128, 16 KB over 128 at
+// 64 x 64, 4 KB over 64 (four float4 each) at 32 x 32; the rectangular heads
+// between them take 64 to 256 threads of eight.  A whole head is one
+// contiguous block, which streams about 7 % faster on MI355X than two
+// 64-column halves of it (rows read as 256-byte pieces at a 512-byte
+// stride), for the append and the fold alike.  At 128 x 128 the decode modes
+// use 256 threads of sixteen float4 each: four heads per CU instead of
+// three, appends 2-4 % faster than with 512 threads of eight.  The
+// decode-and-fold keeps the append's shape, so that per-slot decode (one
+// kernel that appends or folds per slot) adds its column sums in the same
+// order as the lockstep kernels and gives the same bits.  At 128 x 128 the
 // standalone fold and the eager kernel keep 512 threads, 1-2 % faster for
 // them; the fold's result does not depend on the shape (no column sums).
-template <int D, int MODE>
+template <int DK, int DV, int MODE>
 struct Shape {
     static constexpr bool WIDE = MODE == MODE_FOLD || MODE == MODE_EAGER;
-    static constexpr int TV = D;
-    static constexpr int NT = D == 128 ? (WIDE ? 512 : 256) : (D == 64 ? 128 : 64);
+    static constexpr int TV = DV;
+    static constexpr int EIGHT = DK * DV / 32;  // threads of eight float4 each
+    static constexpr int BASE = EIGHT > 256 ? 256 : EIGHT;
+    static constexpr int NT0 = BASE > DV ? BASE : DV;
+    static constexpr int NT1 = NT0 > 64 ? NT0 : 64;
+    static constexpr int NT = (DK == 128 && DV == 128 && WIDE) ? 512 : NT1;
 };
 
 // Workgroups are handed to the eight XCDs round-robin in dispatch order
@@ -222,10 +230,10 @@ __device__ __forceinline__ float column_sum_valu(float x) {
 // afterwards) and the value input of the column stage -- is issued first,
 // with no branch and no dependence between them, so that one memory
 // round-trip covers them all; only then does any arithmetic start.
-template <int OP, typename TIn, int D, int TV, int NT, int MODE, int CMAX>
+template <int OP, typename TIn, int DK, int DV, int TV, int NT, int MODE, int CMAX>
 __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     const StepParams p) {
-    using G = Geom<D, TV, NT>;
+    using G = Geom<DK, DV, TV, NT>;
     constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
     constexpr int KL = G::KL, EPP = G::EPP;
     constexpr bool GDN = OP == OP_GDN;
@@ -244,13 +252,15 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     using Raw = typename In4<TIn>::raw;
     using RawX = typename In4<TX>::raw;
     static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
+    // split replay: the record's scaled key and query, PMV floats per thread
+    constexpr int PMV = (2 * DK + NT - 1) / NT;
 
-    __shared__ __attribute__((aligned(16))) float s_mv0[D];    // khat (delta rules)
-    __shared__ __attribute__((aligned(16))) float s_mv1[D];    // qhat, or rhat (RWKV6)
-    __shared__ __attribute__((aligned(16))) float s_scale[D];  // factor on each base row when writing
-    __shared__ __attribute__((aligned(16))) float s_krow[D];   // current key, per row
-    __shared__ __attribute__((aligned(16))) float s_wrow[D];   // RWKV6: current decay, per row
-    __shared__ __attribute__((aligned(16))) float s_kt[LOGGED ? CP * D : 4];  // [entry][row] decayed keys
+    __shared__ __attribute__((aligned(16))) float s_mv0[DK];    // khat (delta rules)
+    __shared__ __attribute__((aligned(16))) float s_mv1[DK];    // qhat, or rhat (RWKV6)
+    __shared__ __attribute__((aligned(16))) float s_scale[DK];  // factor on each base row when writing
+    __shared__ __attribute__((aligned(16))) float s_krow[DK];   // current key, per row
+    __shared__ __attribute__((aligned(16))) float s_wrow[DK];   // RWKV6: current decay, per row
+    __shared__ __attribute__((aligned(16))) float s_kt[LOGGED ? CP * DK : 4];  // [entry][row] decayed keys
     __shared__ __attribute__((aligned(16))) float s_x[LOGGED && CAN_WRITE ? CP * TV : 4];  // [entry][tile col]
     __shared__ float s_coef[2][CP];  // replay coefficients: k side, q/r side
     __shared__ __attribute__((aligned(16))) float s_red[NW][2][TV];
@@ -298,17 +308,17 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     TIn vraw = {};
     if (TOKEN) {
         if (!PREPPED) {
-            kraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.k) + (size_t)n * D + c4);
-            qraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.q) + (size_t)n * D + c4);
+            kraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.k) + (size_t)n * DK + c4);
+            qraw = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.q) + (size_t)n * DK + c4);
             if (GDN)
                 alpha = p.decay[n];
             else
-                dec4 = *reinterpret_cast<const f4 *>(p.decay + (size_t)n * D + c4);
+                dec4 = *reinterpret_cast<const f4 *>(p.decay + (size_t)n * DK + c4);
         }
         if (DELTA && !PREP) beta = p.beta[n];
         if (OP == OP_RWKV6 && !PREPPED)
-            bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * D + c4);
-        if (!PREP) vraw = static_cast<const TIn *>(p.v)[(size_t)n * D + col0 + tid % TV];  // used by tid < TV
+            bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * DK + c4);
+        if (!PREP) vraw = static_cast<const TIn *>(p.v)[(size_t)n * DV + col0 + tid % TV];  // used by tid < TV
     }
     // A2. The log: cumulative log-decay of the newest entry, the key side of
     //     this thread's entries and, in the thread's own row slots (entries
@@ -324,52 +334,56 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         if (GDN)
             glast_s = p.logG[el];
         else
-            glast4 = *reinterpret_cast<const f4 *>(p.logG + el * D + c4);
+            glast4 = *reinterpret_cast<const f4 *>(p.logG + el * DK + c4);
 #pragma unroll
         for (int ps = 0; ps < KPASS; ++ps) {
             const size_t e = (size_t)n * C + min(ps * EPP + ke, last);
-            klog[ps] = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.logK) + e * D + c4);
+            klog[ps] = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.logK) + e * DK + c4);
             if (GDN)
                 glog_s[ps] = p.logG[e];
             else
-                glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * D + c4);
+                glog4[ps] = *reinterpret_cast<const f4 *>(p.logG + e * DK + c4);
         }
     }
     if (LOGGED && !PREP) {
-        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * D + col0 + 4 * cg;
+        const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * DV + col0 + 4 * cg;
 #pragma unroll
         for (int j = 0; j < XR; ++j)
-            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * D);
+            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * DV);
     }
-    // A2'. Split replay: this head's prep record (thread t < 2D takes float t
-    //      of the scaled key | scaled query, and one coefficient).
-    float pre_mv = 0.f, pre_coef = 0.f, pre_dot = 0.f;
+    // A2'. Split replay: this head's prep record (thread t takes floats t,
+    //      t + NT, ... of the scaled key | scaled query, and one coefficient).
+    float pre_mv[PMV], pre_coef = 0.f, pre_dot = 0.f;
     if (PREPPED) {
-        static_assert(!PREPPED || 2 * D <= NT, "one record float of the scaled vectors per thread");
-        const float *rec = p.prep + (size_t)n * prep_stride(D, CMAX);
-        pre_mv = rec[min(tid, 2 * D - 1)];
-        pre_coef = rec[2 * D + tid % (2 * CP)];
-        pre_dot = rec[2 * D + 2 * CP];
+        const float *rec = p.prep + (size_t)n * prep_stride(DK, CMAX);
+#pragma unroll
+        for (int m = 0; m < PMV; ++m) pre_mv[m] = rec[min(tid + m * NT, 2 * DK - 1)];
+        pre_coef = rec[2 * DK + tid % (2 * CP)];
+        pre_dot = rec[2 * DK + 2 * CP];
     }
 
     // A3. The base tile: nearly all of the traffic, issued last so that the
     //     key-side preparation below, which waits only for the small loads
     //     above (loads complete in issue order), overlaps the tile's flight.
-    //     Row r of the tile is TV/4 float4 at head offset r*D/4 + col0/4.
-    const size_t tile4 = (size_t)n * (D * D / 4) + col0 / 4 + (size_t)rs * (D / 4) + cg;
+    //     Row r of the tile is TV/4 float4 at head offset r*DV/4 + col0/4.
+    const size_t tile4 = (size_t)n * (DK * DV / 4) + col0 / 4 + (size_t)rs * (DV / 4) + cg;
     const f4 *src4 = reinterpret_cast<const f4 *>(p.base) + tile4;
     f4 s[R];
     if (!PREP) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (D / 4));
+        for (int i = 0; i < R; ++i) s[i] = __builtin_nontemporal_load(src4 + (size_t)i * RPP * (DV / 4));
     }
 
     // ---------------- Phase B: key-side preparation into LDS ----------------
     if constexpr (PREPPED) {
-        if (tid < D)
-            s_mv0[tid] = pre_mv;
-        else if (tid < 2 * D)
-            s_mv1[tid - D] = pre_mv;
+#pragma unroll
+        for (int m = 0; m < PMV; ++m) {
+            const int idx = tid + m * NT;
+            if (idx < DK)
+                s_mv0[idx] = pre_mv[m];
+            else if (idx < 2 * DK)
+                s_mv1[idx - DK] = pre_mv[m];
+        }
         if (tid < 2 * CP) (&s_coef[0][0])[tid] = pre_coef;
         if (tid == 0) s_dot = pre_dot;
     } else {
@@ -408,17 +422,17 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         *reinterpret_cast<f4 *>(&s_scale[c4]) = sc;
         *reinterpret_cast<f4 *>(&s_krow[c4]) = k;
         *reinterpret_cast<f4 *>(&s_wrow[c4]) = dv;
-        if (LOGGED && CAN_WRITE && cur_in_log) *reinterpret_cast<f4 *>(&s_kt[L * D + c4]) = k;
+        if (LOGGED && CAN_WRITE && cur_in_log) *reinterpret_cast<f4 *>(&s_kt[L * DK + c4]) = k;
     }
     // append the token's key side as entry L (one writer per value; tile 0)
     if (append && tile == 0 && ke == 0) {
         const size_t e = (size_t)n * C + L;
-        *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * D + c4) = kraw;
-        if (!GDN) *reinterpret_cast<f4 *>(p.logG + e * D + c4) = gn;
+        *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * DK + c4) = kraw;
+        if (!GDN) *reinterpret_cast<f4 *>(p.logG + e * DK + c4) = gn;
     }
     if (append && GDN && tile == 0 && tid == 0) p.logG[(size_t)n * C + L] = gn.x;
     if (TOKEN) {
-        // every key-side group holds all D channels, so each group's sum is complete
+        // every key-side group holds all DK channels, so each group's sum is complete
         float part = DELTA ? dot4(k, q) : dot4(q * bon4, k);
         part = group_sum_valu<KL>(part);
         if (tid == 0) s_dot = part;
@@ -439,7 +453,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             if (!valid) kt = f4{0.f, 0.f, 0.f, 0.f};
             pk[ps] = dot4(kt, k);
             pq[ps] = dot4(kt, q);
-            if (CAN_WRITE && writes && valid) *reinterpret_cast<f4 *>(&s_kt[i * D + c4]) = kt;
+            if (CAN_WRITE && writes && valid) *reinterpret_cast<f4 *>(&s_kt[i * DK + c4]) = kt;
         }
         if (TOKEN) {
 #pragma unroll
@@ -468,12 +482,13 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         }
         // zero the slots between the last folded entry and the next multiple of four
         if (CAN_WRITE && writes) {
+            constexpr int W = DK > TV ? DK : TV;
             const int ne = cur_in_log ? L + 1 : L;
             const int pad = ((ne + 3) & ~3) - ne;
-            for (int idx = tid; idx < pad * D; idx += NT) {
-                const int i = ne + idx / D;
-                const int c = idx % D;
-                s_kt[i * D + c] = 0.f;
+            for (int idx = tid; idx < pad * W; idx += NT) {
+                const int i = ne + idx / W;
+                const int c = idx % W;
+                if (c < DK) s_kt[i * DK + c] = 0.f;
                 if (c < TV) s_x[i * TV + c] = 0.f;
             }
         }
@@ -483,14 +498,14 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
 
     if constexpr (PREP) {
         // split replay, first stage: store the record and leave
-        float *rec = p.prep + (size_t)n * prep_stride(D, CMAX);
-        static_assert(!PREP || 2 * D <= NT, "one record float of the scaled vectors per thread");
-        if (tid < 2 * D && (DELTA || tid >= D)) rec[tid] = tid < D ? s_mv0[tid] : s_mv1[tid - D];
+        float *rec = p.prep + (size_t)n * prep_stride(DK, CMAX);
+        for (int idx = tid; idx < 2 * DK; idx += NT)
+            if (DELTA || idx >= DK) rec[idx] = idx < DK ? s_mv0[idx] : s_mv1[idx - DK];
         if (tid < L) {
-            rec[2 * D + tid] = s_coef[0][tid];
-            rec[2 * D + CP + tid] = s_coef[1][tid];
+            rec[2 * DK + tid] = s_coef[0][tid];
+            rec[2 * DK + CP + tid] = s_coef[1][tid];
         }
-        if (tid == 0) rec[2 * D + 2 * CP] = s_dot;
+        if (tid == 0) rec[2 * DK + 2 * CP] = s_dot;
         return;
     }
 
@@ -546,13 +561,13 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
                 xnew = vj;
                 o = zj + s_dot * vj;
             }
-            p.out[(size_t)n * D + j] = o;
+            p.out[(size_t)n * DV + j] = o;
             if (append) {
                 const size_t e = (size_t)n * C + L;
                 if (DELTA)
-                    static_cast<float *>(p.logX)[e * D + j] = xnew;
+                    static_cast<float *>(p.logX)[e * DV + j] = xnew;
                 else
-                    static_cast<TIn *>(p.logX)[e * D + j] = vraw;
+                    static_cast<TIn *>(p.logX)[e * DV + j] = vraw;
             }
             if (LOGGED && CAN_WRITE && cur_in_log)
                 s_x[L * TV + jt] = xnew;
@@ -579,8 +594,8 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
                     const int row = rs + RPP * i;
-                    acc[i] += s_kt[(e + 0) * D + row] * x0 + s_kt[(e + 1) * D + row] * x1 +
-                              s_kt[(e + 2) * D + row] * x2 + s_kt[(e + 3) * D + row] * x3;
+                    acc[i] += s_kt[(e + 0) * DK + row] * x0 + s_kt[(e + 1) * DK + row] * x1 +
+                              s_kt[(e + 2) * DK + row] * x2 + s_kt[(e + 3) * DK + row] * x3;
                 }
             }
         }
@@ -597,7 +612,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         }
         f4 *dst4 = reinterpret_cast<f4 *>(p.dst) + tile4;
 #pragma unroll
-        for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RPP * (D / 4));
+        for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RPP * (DV / 4));
     }
 }
 

@@ -9,12 +9,12 @@ minimum -- every input, log entry and state element read or written once --
 which is what "achieved GB/s" divides by.  The C library's
 dl_predict_token_us / dl_choose_capacity implement the same model.
 
-Per head, D = dk = dv, s = input element size (4 fp32, 2 bf16):
-  base tile        4 D^2
-  token inputs     q|r, k, v: 3 D s; beta 4 (delta rules); decay 4 (GDN) or 4 D
-  output           4 D
-  log entry        X: 4 D (u, delta rules) or D s (v, RWKV6); K: D s; G: 4 or 4 D
-  RWKV6 bonus      4 D per attention head, read once per launch (H rows)
+Per head, dk key and dv value channels, s = input element size (4 fp32, 2 bf16):
+  base tile        4 dk dv
+  token inputs     q|r, k: 2 dk s; v: dv s; beta 4 (delta rules); decay 4 (GDN) or 4 dk
+  output           4 dv
+  log entry        X: 4 dv (u, delta rules) or dv s (v, RWKV6); K: dk s; G: 4 or 4 dk
+  RWKV6 bonus      4 dk per attention head, read once per launch (H rows)
 An append at log length L reads the base, the token and L entries and writes
 one entry and the output; the fused fold (L = C-1) also writes the base and
 writes no entry; eager reads and writes the state.
@@ -27,35 +27,44 @@ class Shape:
     op: str
     B: int
     H: int
-    d: int
+    d: int         # key width dk (and the value width when dv is 0)
     in_bytes: int  # 4 (fp32) or 2 (bf16)
+    dv: int = 0    # value width; 0 means dv = d
 
     @property
     def heads(self):
         return self.B * self.H
 
+    @property
+    def dk(self):
+        return self.d
+
+    @property
+    def dvv(self):
+        return self.dv or self.d
+
     def base(self):
-        return 4 * self.d * self.d
+        return 4 * self.dk * self.dvv
 
     def token_in(self):
-        d, s = self.d, self.in_bytes
-        b = 3 * d * s
+        s = self.in_bytes
+        b = (2 * self.dk + self.dvv) * s
         if self.op != "rwkv6":
             b += 4  # beta
-        b += 4 if self.op == "gdn" else 4 * d
+        b += 4 if self.op == "gdn" else 4 * self.dk
         return b
 
     def out(self):
-        return 4 * self.d
+        return 4 * self.dvv
 
     def entry(self):
-        d, s = self.d, self.in_bytes
-        x = d * s if self.op == "rwkv6" else 4 * d
-        g = 4 if self.op == "gdn" else 4 * d
-        return x + d * s + g
+        s = self.in_bytes
+        x = self.dvv * s if self.op == "rwkv6" else 4 * self.dvv
+        g = 4 if self.op == "gdn" else 4 * self.dk
+        return x + self.dk * s + g
 
     def shared(self):
-        return 4 * self.d * self.H if self.op == "rwkv6" else 0
+        return 4 * self.dk * self.H if self.op == "rwkv6" else 0
 
 
 def append_bytes(sh: Shape, L: int) -> int:
@@ -132,6 +141,6 @@ def per_token_bytes(sh: Shape, C: int) -> float:
 def cycle_flops(sh: Shape, C: int) -> int:
     """Useful FLOPs of one cycle: the base mat-vecs (two for delta rules, one
     for RWKV6) every token, plus the rank-C fold and row scaling once."""
-    mv = (4 if sh.op != "rwkv6" else 2) * sh.d * sh.d
-    fold = 2 * C * sh.d * sh.d + sh.d * sh.d
+    mv = (4 if sh.op != "rwkv6" else 2) * sh.dk * sh.dvv
+    fold = 2 * C * sh.dk * sh.dvv + sh.dk * sh.dvv
     return sh.heads * (C * mv + fold)

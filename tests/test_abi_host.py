@@ -16,7 +16,8 @@ from recurrent_state_updates_amd import _binding as B
 from recurrent_state_updates_amd import build as dlbuild
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "deltalog.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 FAKE = 0x7F0000000000  # 256-byte aligned, never dereferenced
 # a fake device layout with no two buffers overlapping: the base at FAKE, the
 # workspace, the token inputs 1 MB apart, the prep records, a materialise dst
@@ -34,15 +35,18 @@ def lib():
 
 
 def declared_functions():
-    with open(HEADER) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(dl_[a-z_]+)\s*\(", text)))
+    names = set()
+    for path in HEADERS:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(dl_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 27, names
     for name in names:
         assert hasattr(lib, name), f"{name} is declared in deltalog.h but not exported"
     for name in names:
@@ -60,17 +64,18 @@ def _round(x):
     return (x + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("op,dtype,d,C", [("gdn", "bf16", 128, 8), ("kda", "bf16", 128, 4),
-                                          ("rwkv6", "bf16", 64, 8), ("gdn", "f32", 32, 4),
-                                          ("rwkv6", "f32", 32, 32)])
-def test_workspace_size_and_layout(op, dtype, d, C):
+@pytest.mark.parametrize("op,dtype,d,dv,C", [("gdn", "bf16", 128, 128, 8), ("kda", "bf16", 128, 128, 4),
+                                             ("rwkv6", "bf16", 64, 64, 8), ("gdn", "f32", 32, 32, 4),
+                                             ("rwkv6", "f32", 32, 32, 32), ("gdn", "bf16", 64, 128, 8),
+                                             ("kda", "f32", 128, 32, 3), ("rwkv6", "bf16", 32, 128, 16)])
+def test_workspace_size_and_layout(op, dtype, d, dv, C):
     Bsz, H = 3, 5
-    cfg = dl.make_config(op, dtype, Bsz, H, d, d, C)
+    cfg = dl.make_config(op, dtype, Bsz, H, d, dv, C)
     n = Bsz * H * C
     isz = 2 if dtype == "bf16" else 4
     xsz = isz if op == "rwkv6" else 4
     gw = 1 if op == "gdn" else d
-    x = _round(n * d * xsz)
+    x = _round(n * dv * xsz)
     k = _round(n * d * isz)
     g = _round(n * gw * 4)
     slots = _round(Bsz * 4) + _round(Bsz)  # per-slot log origin and active flag
@@ -82,7 +87,8 @@ def test_workspace_size_and_layout(op, dtype, d, C):
     (dict(op=7), B.DL_ERR_ARG), (dict(in_dtype=5), B.DL_ERR_ARG),
     (dict(B=0), B.DL_ERR_SHAPE), (dict(H=-1), B.DL_ERR_SHAPE),
     (dict(C=0), B.DL_ERR_SHAPE), (dict(C=33), B.DL_ERR_SHAPE),
-    (dict(dk=128, dv=64), B.DL_ERR_UNSUPPORTED), (dict(dk=96, dv=96), B.DL_ERR_UNSUPPORTED),
+    (dict(dk=128, dv=48), B.DL_ERR_UNSUPPORTED), (dict(dk=96, dv=96), B.DL_ERR_UNSUPPORTED),
+    (dict(dk=16, dv=64), B.DL_ERR_UNSUPPORTED),
     (dict(B=(1 << 22) + 1, H=2, dk=32, dv=32), B.DL_ERR_SHAPE), (dict(B=1 << 30, H=1 << 30), B.DL_ERR_SHAPE),
 ])
 def test_invalid_configs(kw, code):
@@ -295,6 +301,9 @@ def test_prep_bytes():
     assert dl.dl_prep_bytes(dl.make_config("kda", "bf16", 2, 4, 64, 64, 17)) == 8 * (128 + 64 + 4) * 4
     assert dl.dl_prep_bytes(dl.make_config("rwkv6", "f32", 128, 32, 64, 64, 8)) == 4096 * (128 + 16 + 4) * 4
     assert dl.dl_prep_bytes(B.Config(0, 1, 2, 4, 48, 48, 4)) == 0
+    # the record holds the scaled key and query: its width is dk, whatever dv is
+    assert dl.dl_prep_bytes(dl.make_config("gdn", "bf16", 2, 4, 128, 32, 8)) == 8 * (256 + 16 + 4) * 4
+    assert dl.dl_prep_bytes(dl.make_config("gdn", "bf16", 2, 4, 32, 128, 8)) == 8 * (64 + 16 + 4) * 4
 
 
 def test_split_replay_and_graph_validate_on_the_host():
@@ -346,3 +355,15 @@ def test_largest_head_count_is_accepted():
     assert B.DL_MAX_HEADS == 1 << 23
     # X (fp32) and K (bf16) for 32 entries of width 32 per head, plus the decays
     assert dl.dl_workspace_bytes(cfg) > (1 << 23) * 32 * 32 * (4 + 2)
+
+
+def test_probe_validates_on_the_host():
+    lib = B.load_library()
+    sink = FAKE + 0x50000000
+    assert lib.dl_probe_stream(2, FAKE, 1, 1, 64, 64, sink, None) == -1          # bad mode
+    assert lib.dl_probe_stream(0, FAKE + 8, 1, 1, 64, 64, sink, None) == -1      # misaligned state
+    assert lib.dl_probe_stream(0, FAKE, 1, 1, 64, 64, 0, None) == -1             # no sink
+    assert lib.dl_probe_stream(1, FAKE, 0, 1, 64, 64, sink, None) == -2          # empty batch
+    assert lib.dl_probe_stream(1, FAKE, 1 << 22, 4, 64, 64, sink, None) == -2    # too many heads
+    assert lib.dl_probe_stream(0, FAKE, 1, 1, 64, 48, sink, None) == -3          # width not built
+    assert "32, 64 or 128" in lib.dl_probe_last_error().decode()

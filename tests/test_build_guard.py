@@ -56,7 +56,7 @@ def test_a_failed_build_leaves_no_library(tmp_path, monkeypatch):
     lib.write_bytes(b"stale")
     monkeypatch.setattr(B, "LIB", str(lib))
     monkeypatch.setattr(B, "BUILD_DIR", str(tmp_path / "_build"))
-    monkeypatch.setattr(B, "SOURCES", ["does_not_exist.hip"])
+    monkeypatch.setattr(B, "SOURCES", [("does_not_exist.hip", "does_not_exist", [])])
     with pytest.raises(RuntimeError):
         B.build()
     assert not lib.exists()

@@ -6,8 +6,8 @@ from recurrent_state_updates_amd import _binding as B
 from recurrent_state_updates_amd import traffic
 
 
-def _predict_py(op, Bsz, H, d, C, read, copy):
-    sh = traffic.Shape(op, Bsz, H, d, 2)
+def _predict_py(op, Bsz, H, d, C, read, copy, dv=0):
+    sh = traffic.Shape(op, Bsz, H, d, 2, dv)
     us = sum(traffic.append_bytes(sh, L) for L in range(C - 1)) / (read * 1e3)
     us += traffic.merge_bytes(sh, C) / (copy * 1e3)
     return us / C
@@ -19,6 +19,16 @@ def test_library_model_matches_the_python_byte_model(op, d, C):
     cfg = dl.make_config(op, "bf16", 96, 32, d, d, C)
     got = dl.dl_predict_token_us(cfg, 6000.0, 5000.0)
     assert got == pytest.approx(_predict_py(op, 96, 32, d, C, 6000.0, 5000.0), rel=1e-12)
+
+
+@pytest.mark.parametrize("op,dk,dv", [("gdn", 64, 128), ("kda", 128, 32), ("rwkv6", 32, 64)])
+def test_model_with_distinct_key_and_value_widths(op, dk, dv):
+    cfg = dl.make_config(op, "bf16", 16, 8, dk, dv, 8)
+    got = dl.dl_predict_token_us(cfg, 6000.0, 5000.0)
+    assert got == pytest.approx(_predict_py(op, 16, 8, dk, 8, 6000.0, 5000.0, dv), rel=1e-12)
+    sh = traffic.Shape(op, 16, 8, dk, 2, dv)
+    assert sh.base() == 4 * dk * dv
+    assert traffic.eager_bytes(sh) == 16 * 8 * (8 * dk * dv + sh.token_in() + 4 * dv) + sh.shared()
 
 
 def test_default_bandwidths_and_argmin():

@@ -90,6 +90,9 @@ def load_library():
         "dl_graph_destroy": (None, [vp]),
         "dl_status_string": (ctypes.c_char_p, [i]),
         "dl_last_error": (ctypes.c_char_p, []),
+        # measurement kernels (include/deltalog_probe.h)
+        "dl_probe_stream": (i, [i, vp, i, i, i, i, vp, vp]),
+        "dl_probe_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -104,6 +107,21 @@ def _check(status):
         lib = load_library()
         msg = lib.dl_last_error().decode() or lib.dl_status_string(status).decode()
         raise DeltaLogError(status, msg)
+
+
+DL_PROBE_READ, DL_PROBE_COPY = 0, 1
+
+
+def dl_probe_last_error():
+    return load_library().dl_probe_last_error().decode()
+
+
+def dl_probe_stream(mode, state, B, H, dk, dv, sink, stream=None):
+    """One launch of a stream-ceiling probe (include/deltalog_probe.h)."""
+    lib = load_library()
+    st = lib.dl_probe_stream(mode, state, B, H, dk, dv, sink, stream)
+    if st != 0:
+        raise DeltaLogError(st, lib.dl_probe_last_error().decode())
 
 
 def make_config(op, in_dtype, B, H, dk, dv, C=1):

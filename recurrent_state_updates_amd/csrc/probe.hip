@@ -1,0 +1,108 @@
+// probe.hip -- what MI355X streams at the access pattern of the decode
+// kernels: the same workgroup per head, thread geometry, XCD mapping and
+// 16-byte nontemporal loads (and stores) as the append and the
+// decode-and-fold, with none of their other work.  These bound the path from
+// above: an append cannot beat a read of its heads, a fold cannot beat an
+// in-place copy of them.
+#include "../../include/deltalog_probe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "step_kernel.h"
+
+namespace dlk {
+
+// COPY = false: read every head once and keep one conditional store, which
+// the compiler cannot drop without the sum (a sum of finite state values
+// equal to NaN never happens).  COPY = true: read and write every head back
+// in place, unchanged.
+template <int DK, int DV, int NT, bool COPY>
+__global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, int N) {
+    using G = Geom<DK, DV, DV, NT>;
+    int n, tile;
+    block_to_tile(blockIdx.x, N, 1, n, tile);
+    const int tid = threadIdx.x;
+    const int cg = tid % G::LPR, rs = tid / G::LPR;
+    f4 *p4 = reinterpret_cast<f4 *>(state) + (size_t)n * (DK * DV / 4) + (size_t)rs * (DV / 4) + cg;
+    f4 s[G::R];
+#pragma unroll
+    for (int i = 0; i < G::R; ++i) s[i] = __builtin_nontemporal_load(p4 + (size_t)i * G::RPP * (DV / 4));
+    if constexpr (COPY) {
+#pragma unroll
+        for (int i = 0; i < G::R; ++i) __builtin_nontemporal_store(s[i], p4 + (size_t)i * G::RPP * (DV / 4));
+    } else {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < G::R; ++i) acc += (s[i].x + s[i].y) + (s[i].z + s[i].w);
+        if (acc != acc) sink[0] = acc;
+    }
+}
+
+template <int DK, int DV>
+hipError_t launch_probe(int copy, float *state, float *sink, int N, hipStream_t s) {
+    constexpr int NT = Shape<DK, DV, MODE_APPEND>::NT;
+    if (copy)
+        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, true>), dim3(N), dim3(NT), 0, s, state, sink, N);
+    else
+        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, false>), dim3(N), dim3(NT), 0, s, state, sink, N);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t probe_value_width(int dv, int copy, float *state, float *sink, int N, hipStream_t s) {
+    switch (dv) {
+        case 32: return launch_probe<DK, 32>(copy, state, sink, N, s);
+        case 64: return launch_probe<DK, 64>(copy, state, sink, N, s);
+        case 128: return launch_probe<DK, 128>(copy, state, sink, N, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dlk
+
+namespace {
+thread_local std::string g_probe_error;
+}
+
+extern "C" {
+
+int dl_probe_stream(int mode, float *state, int B, int H, int dk, int dv, float *sink, void *stream) {
+    auto built = [](int w) { return w == 32 || w == 64 || w == 128; };
+    if (mode != DL_PROBE_READ && mode != DL_PROBE_COPY) {
+        g_probe_error = "mode must be DL_PROBE_READ or DL_PROBE_COPY";
+        return -1;
+    }
+    if (!state || !sink || (reinterpret_cast<uintptr_t>(state) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u)) {
+        g_probe_error = "state (16-byte aligned) and sink (4-byte aligned) must be non-NULL";
+        return -1;
+    }
+    if (B <= 0 || H <= 0 || (size_t)B * (size_t)H > (size_t)(1 << 23)) {
+        g_probe_error = "B and H must be positive with B * H <= 2^23";
+        return -2;
+    }
+    if (!built(dk) || !built(dv)) {
+        g_probe_error = "dk and dv must each be 32, 64 or 128";
+        return -3;
+    }
+    const int N = B * H;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int copy = mode == DL_PROBE_COPY;
+    hipError_t e;
+    switch (dk) {
+        case 32: e = dlk::probe_value_width<32>(dv, copy, state, sink, N, s); break;
+        case 64: e = dlk::probe_value_width<64>(dv, copy, state, sink, N, s); break;
+        default: e = dlk::probe_value_width<128>(dv, copy, state, sink, N, s); break;
+    }
+    if (e != hipSuccess) {
+        g_probe_error = std::string("kernel launch failed: ") + hipGetErrorString(e);
+        return -4;
+    }
+    g_probe_error.clear();
+    return 0;
+}
+
+const char *dl_probe_last_error(void) { return g_probe_error.c_str(); }
+
+}  // extern "C"

@@ -12,8 +12,15 @@ Printed: ONE JSON line.  Besides the contract fields it carries
                 events recorded around every launch of the timed region
   cpu_baseline  the fp64 oracle timed on the host cores on a bounded sample
   eager         this library's eager dense kernel on the same inputs
+  cold          every launch of a few cycles timed alone after the 256 MB
+                Infinity Cache was refilled with another buffer (the state of
+                the other layers of a model would pass through it between two
+                launches of one layer)
+  ceilings      what the GPU streams at the kernels' own access pattern: a read
+                and an in-place copy of every head with the decode kernels'
+                workgroup shape, mapping and loads, back to back and cold
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--C c]
-                       [--cold] [--report PATH] [--no-cpu]
+                       [--no-cold] [--report PATH] [--no-cpu] [--capacity-study]
 """
 import argparse
 import hashlib
@@ -37,17 +44,21 @@ def metric_name(op, B, H, dk, dv, C):
     return METRIC_TEMPLATE.format(op=op.upper(), B=B, H=H, d=d, C=C)
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "append_gdn_b128_h32_d128_c8_traffic.md")
+# committed counter summaries of the append, per serving-shape workload at C = 8
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "append_{workload}_c8_traffic.md")
+# the sources each kind of counter summary is tied to
 KERNEL_SOURCES = ["recurrent_state_updates_amd/csrc/step_kernel.h",
                   "recurrent_state_updates_amd/csrc/launch.h"]
+CHUNK_SOURCES = KERNEL_SOURCES + ["recurrent_state_updates_amd/csrc/chunk_kernel.h"]
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=None):
     """First 16 hex digits of the SHA-256 of the kernel sources with comments
     and blank space removed: the counters are tied to the code, not to its
-    commentary."""
+    commentary.  The single-token summaries hash step_kernel.h and launch.h,
+    the multi-token ones chunk_kernel.h as well (CHUNK_SOURCES)."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel)) as f:
             text = f.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -56,12 +67,14 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_bytes):
-    """HBM bytes per append launch from the committed rocprofv3 counter summary,
-    or None when there is none or the kernel source changed since."""
-    if not os.path.exists(TRAFFIC_PROFILE):
+def measured_traffic(workload):
+    """HBM bytes per append launch from the committed rocprofv3 counter summary
+    of the workload at C = 8, or None when there is none or the kernel source
+    changed since."""
+    path = TRAFFIC_PROFILE.format(workload=workload)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_PROFILE) as f:
+    with open(path) as f:
         text = f.read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
@@ -79,7 +92,12 @@ def parse():
     ap.add_argument("--C", type=int, default=8, help="log capacity = merge interval")
     ap.add_argument("--B", type=int, default=None, help="override the batch (sweep)")
     ap.add_argument("--cold", action="store_true",
-                    help="also time each launch after flushing the 256 MB Infinity Cache")
+                    help="(the default) time each launch of a few cycles alone after refilling the 256 MB "
+                         "Infinity Cache with another buffer")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache timing and the ceilings")
+    ap.add_argument("--capacity-study", action="store_true",
+                    help="also time the log capacity dl_choose_capacity picks (with the measured ceilings as "
+                         "its bandwidths) beside C=8 and C=16, each against the model's prediction")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-eager", action="store_true", help="skip the eager GPU kernel")
     ap.add_argument("--cpu-tokens", type=int, default=256, help="tokens in the CPU-baseline sample")
@@ -216,7 +234,7 @@ def main():
         dom_us = merge_us
         dom_name = "decode_fold"
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    measured = measured_traffic(dom_bytes) if (w.name == "gdn_b128_h32_d128" and C == 8 and Bsz == 128) else None
+    measured = measured_traffic(w.name) if (C == 8 and Bsz == w.B) else None
 
     result = {
         "metric": metric_name(w.op, Bsz, H, D, D, C),
@@ -334,8 +352,25 @@ def main():
         result["calibration_copy_bytes"] = int(src.numel() * 4)
         del src, dst
 
-    if args.cold:
-        result["cold"] = cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, args.tokens)
+    if not args.no_cold:
+        flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        ceil = stream_ceilings(dl, d["S0"], Bsz, H, D, D, stream, flush, K)
+        result["ceilings"] = ceil
+        cold = cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, args.tokens, flush)
+        cold["frac_of_peak"] = round(cold["achieved_GBps"] / PEAK_HBM_GBPS, 4)
+        cold["isolated"]["frac_of_peak"] = round(cold["isolated"]["achieved_GBps"] / PEAK_HBM_GBPS, 4)
+        if C > 1:
+            app_cold = float(np.mean(cold["append_by_L"]))
+            cold["append_mean_us"] = round(app_cold, 2)
+            cold["append_frac_of_read_ceiling"] = round(ceil["read"]["cold_us"] / app_cold, 4)
+        cold["decode_fold_frac_of_copy_ceiling"] = round(ceil["copy"]["cold_us"] / cold["decode_fold"], 4)
+        result["cold"] = cold
+        if C > 1:
+            result["roofline"]["frac_of_read_ceiling"] = round(ceil["read"]["warm_us"] / dom_us, 4)
+        del flush
+
+    if args.capacity_study and not args.no_cold:
+        result["capacity_study"] = capacity_study(dl, d, w, Bsz, sh, traffic, stream, outs, K, ceil)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(x, w, Bsz, args.cpu_tokens)
@@ -543,68 +578,215 @@ def staggered_multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs
             "achieved_GBps": round(nbytes / ntoks / (wall_us * 1e-6) / 1e9, 1)}
 
 
-def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, ntok=0):
-    """Per-launch event times with a 512 MB read between launches, outside the
-    events: the read refills the 256 MB Infinity Cache with clean lines of
-    another buffer, so each launch finds none of its data cached (a write
-    would leave dirty lines whose write-back the next launch would pay)."""
+def stream_ceilings(dl, S0, Bsz, H, dk, dv, stream, flush, K):
+    """The read and the in-place copy of every head at the decode kernels'
+    access pattern (dl_probe_stream), on a copy of the state: back to back
+    (mean over 4 K launches between two events, as the timed region runs the
+    kernels) and cold, in sequence and isolated (ColdTimer, medians of 12)."""
     import numpy as np
     import torch
-    flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-    sink = torch.empty((), dtype=torch.float32, device=dev)
-    torch.sum(flush, dim=0, out=sink)
+    state = S0.clone()
+    sink = torch.zeros(1, dtype=torch.float32, device=S0.device)
+    sptr = stream.cuda_stream
+    nbytes = Bsz * H * dk * dv * 4
+    timer = ColdTimer(torch, stream, flush)
+    res = {"state_bytes": nbytes}
+    for name, mode, moved in (("read", dl.DL_PROBE_READ, nbytes), ("copy", dl.DL_PROBE_COPY, 2 * nbytes)):
+        def launch():
+            dl.dl_probe_stream(mode, state.data_ptr(), Bsz, H, dk, dv, sink.data_ptr(), sptr)
+        for _ in range(3):
+            launch()
+        n = 4 * K
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        warm = e0.elapsed_time(e1) * 1e3 / n
+        iso = float(np.median([timer.isolated(launch) for _ in range(12)]))
+        raw = float(np.median([timer.paired(launch) for _ in range(12)]))
+        cold = raw - timer.refill_cost()
+        res[name] = {"bytes": moved, "warm_us": round(warm, 2), "warm_GBps": round(moved / (warm * 1e-6) / 1e9, 1),
+                     "cold_us": round(cold, 2), "cold_GBps": round(moved / (cold * 1e-6) / 1e9, 1),
+                     "isolated_cold_us": round(iso, 2),
+                     "isolated_cold_GBps": round(moved / (iso * 1e-6) / 1e9, 1)}
+    assert torch.equal(state, S0), "the copy probe must leave the state unchanged"
+    # the fixed cost of a launch: the read probe over one head, back to back and isolated
+    def one():
+        dl.dl_probe_stream(dl.DL_PROBE_READ, state.data_ptr(), 1, 1, dk, dv, sink.data_ptr(), sptr)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(50):
+        one()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    res["one_head_launch_us"] = {"back_to_back": round(e0.elapsed_time(e1) * 1e3 / 50, 2),
+                                 "isolated_cold": round(float(np.median([timer.isolated(one) for _ in range(12)])), 2)}
+    del state
+    return res
+
+
+def capacity_study(dl, d, w, Bsz, sh, traffic, stream, outs, K, ceil):
+    """NEXT-3 checked on the GPU: the capacity dl_choose_capacity picks when
+    its bandwidths are the measured ceilings (appends at the read rate, the
+    fold at the copy rate), timed beside C = 8 and C = 16 -- back to back, K
+    cycles each -- with the model's prediction for each."""
+    import ctypes
+    import torch
+    read_gbps = ceil["read"]["warm_GBps"]
+    copy_gbps = ceil["copy"]["warm_GBps"]
+    cfg = dl.make_config(w.op, w.in_dtype, Bsz, w.H, w.d, w.d, 8)
+    pick = dl.dl_choose_capacity(cfg, dl.DL_MAX_CAPACITY, read_gbps, copy_gbps)
+    fn = dl.load_library().dl_decode_step
+    sptr = stream.cuda_stream
+    rows = {}
+    for C in sorted({pick, 8, 16}):
+        base = d["S0"].clone()
+        st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
+        refs = [ctypes.byref(st.step_args(d["q"][t], d["k"][t], d["v"][t],
+                                          None if d["beta"] is None else d["beta"][t], d["decay"][t],
+                                          d["bonus"], outs[t])) for t in range(w.T)]
+        ntok = C * max(K, -(-64 // C))  # whole cycles, at least 64 tokens
+        for i in range(2 * C):
+            assert fn(st.handle, refs[i % w.T], sptr) == 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(ntok):
+            assert fn(st.handle, refs[i % w.T], sptr) == 0
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / ntok
+        st.close()
+        model = dl.dl_predict_token_us(dl.make_config(w.op, w.in_dtype, Bsz, w.H, w.d, w.d, C), read_gbps, copy_gbps)
+        rows[str(C)] = {"measured_us_per_token": round(us, 3), "model_us_per_token": round(model, 3),
+                        "measured_over_model": round(us / model, 4)}
+    return {"bandwidths_GBps": {"append_read": read_gbps, "fold_copy": copy_gbps}, "chosen_C": pick,
+            "by_C": rows,
+            "chosen_is_fastest_measured": min(rows, key=lambda c: rows[c]["measured_us_per_token"]) == str(pick)}
+
+
+class ColdTimer:
+    """Launch times with the 256 MB Infinity Cache refilled before each launch
+    by a 512 MB read of another buffer (a read leaves only clean lines, so the
+    launch pays no write-back of the refill).  Two measures:
+
+      isolated     refill, then events around the launch alone: the launch
+                   then also pays the idle GPU's wake-up from the events
+                   (an empty kernel costs about 6 us this way, against about
+                   2 us back to back)
+      in sequence  events around [refill, launch], less the median of events
+                   around [refill] alone (measured after every pair): the
+                   launch's cold cost inside a stream of other work, as a
+                   layer of a model meets it
+    """
+
+    def __init__(self, torch, stream, flush):
+        self.torch, self.stream, self.flush = torch, stream, flush
+        self.sink = torch.empty((), dtype=torch.float32, device=flush.device)
+        self.refill_alone = []
+        self.refill()
+        torch.cuda.synchronize()
+
+    def refill(self):
+        self.torch.sum(self.flush, dim=0, out=self.sink)
+
+    def _events(self):
+        return (self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True))
+
+    def isolated(self, launch):
+        a, b = self._events()
+        self.refill()
+        a.record(self.stream)
+        launch()
+        b.record(self.stream)
+        self.torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3
+
+    def paired(self, launch):
+        """Raw time of [refill, launch]; call refill_cost() at the end."""
+        a, b = self._events()
+        a.record(self.stream)
+        self.refill()
+        launch()
+        b.record(self.stream)
+        self.torch.cuda.synchronize()
+        raw = a.elapsed_time(b) * 1e3
+        c, d = self._events()
+        c.record(self.stream)
+        self.refill()
+        d.record(self.stream)
+        self.torch.cuda.synchronize()
+        self.refill_alone.append(c.elapsed_time(d) * 1e3)
+        return raw
+
+    def refill_cost(self):
+        import numpy as np
+        return float(np.median(self.refill_alone))
+
+
+def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, ntok=0, flush=None):
+    """Every launch of a few merge cycles with the Infinity Cache refilled
+    before it (ColdTimer): in sequence (the headline cold figure) and
+    isolated; the same for calls of ntok tokens."""
+    import numpy as np
+    import torch
+    if flush is None:
+        flush = torch.ones(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    timer = ColdTimer(torch, stream, flush)
     base = d["S0"].clone()
     st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
     ncyc = 6
-    lat = np.zeros((ncyc, C))
+    iso = np.zeros((ncyc, C))
+    raw = np.zeros((ncyc, C))
     tok = 0
-    for c in range(ncyc):
+    for c in range(2 * ncyc):
         for i in range(C):
-            torch.sum(flush, dim=0, out=sink)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
             t = tok % w.T
-            e0.record(stream)
-            st.step(d["q"][t], d["k"][t], d["v"][t], None if d["beta"] is None else d["beta"][t],
-                    d["decay"][t], d["bonus"], outs[t])
-            e1.record(stream)
-            torch.cuda.synchronize()
-            lat[c, i] = e0.elapsed_time(e1) * 1e3
+
+            def launch():
+                st.step(d["q"][t], d["k"][t], d["v"][t], None if d["beta"] is None else d["beta"][t],
+                        d["decay"][t], d["bonus"], outs[t])
+            if c < ncyc:
+                iso[c, i] = timer.isolated(launch)
+            else:
+                raw[c - ncyc, i] = timer.paired(launch)
             tok += 1
     st.close()
-    per_tok = float(np.median(lat.sum(axis=1))) / C
+    seq = raw - timer.refill_cost()
+    per_tok = float(np.median(seq.sum(axis=1))) / C
+    per_tok_iso = float(np.median(iso.sum(axis=1))) / C
+    tok_bytes = traffic.per_token_bytes(sh, C)
     result = {"us_per_token": round(per_tok, 3),
-              "achieved_GBps": round(traffic.per_token_bytes(sh, C) / (per_tok * 1e-6) / 1e9, 1),
-              "append_by_L": [round(float(np.median(lat[:, L])), 2) for L in range(C - 1)],
-              "decode_fold": round(float(np.median(lat[:, C - 1])), 2)}
+              "achieved_GBps": round(tok_bytes / (per_tok * 1e-6) / 1e9, 1),
+              "append_by_L": [round(float(np.median(seq[:, L])), 2) for L in range(C - 1)],
+              "decode_fold": round(float(np.median(seq[:, C - 1])), 2),
+              "refill_us": round(timer.refill_cost(), 2),
+              "isolated": {"us_per_token": round(per_tok_iso, 3),
+                           "achieved_GBps": round(tok_bytes / (per_tok_iso * 1e-6) / 1e9, 1),
+                           "append_by_L": [round(float(np.median(iso[:, L])), 2) for L in range(C - 1)],
+                           "decode_fold": round(float(np.median(iso[:, C - 1])), 2)}}
     if ntok > 1:
-        # the same for calls of ntok tokens, one launch each.  As above, the
-        # refill is queued ahead of the first event without waiting, so that
-        # the host has issued the launch by the time the refill ends.
+        # the same for calls of ntok tokens, one launch each, in sequence
         base = d["S0"].clone()
         st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
         fn = dl.load_library().dl_decode_tokens
         one = [st.step_args(d["q"][t], d["k"][t], d["v"][t], None if d["beta"] is None else d["beta"][t],
                             d["decay"][t], d["bonus"], outs[t]) for t in range(w.T)]
         ncalls = max(4, ncyc * C // ntok)
-        lat_mt, tok, L = [], 0, 0
+        raw_mt, tok, L = [], 0, 0
         nbytes = 0
         for _ in range(ncalls):
             arr = (dl.StepArgs * ntok)(*[one[(tok + i) % w.T] for i in range(ntok)])
-            torch.sum(flush, dim=0, out=sink)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            assert fn(st.handle, arr, ntok, stream.cuda_stream) == 0
-            e1.record(stream)
-            torch.cuda.synchronize()
-            lat_mt.append(e0.elapsed_time(e1) * 1e3)
+            raw_mt.append(timer.paired(lambda: fn(st.handle, arr, ntok, stream.cuda_stream)))
             nbytes += traffic.call_bytes(sh, L, ntok, C)
             L = (L + ntok) % C
             tok += ntok
         st.close()
-        per_tok_mt = sum(lat_mt) / (ncalls * ntok)
+        per_tok_mt = (float(np.sum(raw_mt)) - ncalls * timer.refill_cost()) / (ncalls * ntok)
         result["multi_token"] = {"tokens_per_call": ntok, "us_per_token": round(per_tok_mt, 3),
                                  "achieved_GBps": round(nbytes / (ncalls * ntok) / (per_tok_mt * 1e-6) / 1e9, 1)}
     return result

@@ -21,11 +21,14 @@ ARCH = "gfx950"
 
 # (source, object name, extra defines): the kernel instantiation units are
 # compiled once per (operator, key width), so that they build in parallel.
+# NO_KERNELS: HIP sources that define device data but no kernel, so the
+# compiler prints no resource remarks for them.
 OPS = {0: "gdn", 1: "kda", 2: "rwkv6"}
 KEY_WIDTHS = (32, 64, 128)
 SOURCES = [("deltalog.cpp", "deltalog", []), ("slots.hip", "slots", []), ("probe.hip", "probe", [])] + [
     (f"kernels_{kind}.hip", f"kernels_{kind}_{OPS[op]}_dk{dk}", [f"-DDLK_OP={op}", f"-DDLK_DK={dk}"])
     for kind in ("step", "chunk") for op in OPS for dk in KEY_WIDTHS]
+NO_KERNELS = set()
 
 # Packed fp32 VALU ops are switched off for all device code; the host pass
 # prints that it does not know the feature, which is harmless.  Matrix-core
@@ -35,6 +38,13 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-I", os.path.join(ROOT, "include")]
+
+
+def _extra_flags():
+    """Extra hipcc flags from DELTALOG_HIPCC_FLAGS (space-separated), for
+    building variants of the kernels' compile-time knobs (such as
+    -DDLK_MIN_WAVES=4) to measure against the default."""
+    return os.environ.get("DELTALOG_HIPCC_FLAGS", "").split()
 
 
 def _hipcc():
@@ -119,14 +129,16 @@ def build(verbose: bool = False, jobs: int = None) -> str:
     for src, name, defines in SOURCES:
         obj = os.path.join(BUILD_DIR, name + ".o")
         objs.append(obj)
-        extra = RESOURCE_REMARKS if src.endswith(".hip") else []
-        cmds.append((name, src, [hipcc, *FLAGS, *defines, *extra, "-c", os.path.join(CSRC, src), "-o", obj]))
+        checked = src.endswith(".hip") and name not in NO_KERNELS
+        extra = RESOURCE_REMARKS if checked else []
+        cmds.append((name, src, [hipcc, *FLAGS, *_extra_flags(), *defines, *extra, "-c", os.path.join(CSRC, src),
+                                 "-o", obj]))
     # the longest units first, so that they do not start last
     order = sorted(cmds, key=lambda c: (not c[0].startswith("kernels_chunk"), not c[0].endswith("dk128")))
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         outs = list(ex.map(lambda c: (c[0], c[1], _run(c[2], verbose)), order))
     for name, src, lines in outs:
-        if src.endswith(".hip"):
+        if src.endswith(".hip") and name not in NO_KERNELS:
             check_resources(name, lines)
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)

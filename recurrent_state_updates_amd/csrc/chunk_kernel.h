@@ -141,7 +141,7 @@ void chunk_kernel(const ChunkParams p) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
     int n, tile;
-    block_to_tile(blockIdx.x, p.N, NTILE, n, tile);
+    block_to_tile<false>(blockIdx.x, p.N, NTILE, n, tile);  // dispatch order (see block_to_tile)
     const int C = p.C;
     // The segment in hand: tokens tb .. tb + K - 1 of the arguments, on a log
     // of L entries, folding it when it fills.

@@ -1,5 +1,5 @@
 // probe.hip -- what MI355X streams at the access pattern of the decode
-// kernels: the same workgroup per head, thread geometry, XCD mapping and
+// kernels: the same workgroup per head, thread geometry, block order and
 // 16-byte nontemporal loads (and stores) as the append and the
 // decode-and-fold, with none of their other work.  These bound the path from
 // above: an append cannot beat a read of its heads, a fold cannot beat an
@@ -17,12 +17,13 @@ namespace dlk {
 // COPY = false: read every head once and keep one conditional store, which
 // the compiler cannot drop without the sum (a sum of finite state values
 // equal to NaN never happens).  COPY = true: read and write every head back
-// in place, unchanged.
+// in place, multiplied by `one` (1.0f at run time: the values do not change,
+// but the compiler cannot drop a store it does not know to be redundant).
 template <int DK, int DV, int NT, bool COPY>
-__global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, int N) {
+__global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, int N, float one) {
     using G = Geom<DK, DV, DV, NT>;
     int n, tile;
-    block_to_tile(blockIdx.x, N, 1, n, tile);
+    block_to_tile<StepOrder<DK, DV>::XCD>(blockIdx.x, N, 1, n, tile);
     const int tid = threadIdx.x;
     const int cg = tid % G::LPR, rs = tid / G::LPR;
     f4 *p4 = reinterpret_cast<f4 *>(state) + (size_t)n * (DK * DV / 4) + (size_t)rs * (DV / 4) + cg;
@@ -31,7 +32,7 @@ __global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, in
     for (int i = 0; i < G::R; ++i) s[i] = __builtin_nontemporal_load(p4 + (size_t)i * G::RPP * (DV / 4));
     if constexpr (COPY) {
 #pragma unroll
-        for (int i = 0; i < G::R; ++i) __builtin_nontemporal_store(s[i], p4 + (size_t)i * G::RPP * (DV / 4));
+        for (int i = 0; i < G::R; ++i) __builtin_nontemporal_store(s[i] * one, p4 + (size_t)i * G::RPP * (DV / 4));
     } else {
         float acc = 0.f;
 #pragma unroll
@@ -44,9 +45,9 @@ template <int DK, int DV>
 hipError_t launch_probe(int copy, float *state, float *sink, int N, hipStream_t s) {
     constexpr int NT = Shape<DK, DV, MODE_APPEND>::NT;
     if (copy)
-        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, true>), dim3(N), dim3(NT), 0, s, state, sink, N);
+        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, true>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
     else
-        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, false>), dim3(N), dim3(NT), 0, s, state, sink, N);
+        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, false>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
     return hipGetLastError();
 }
 

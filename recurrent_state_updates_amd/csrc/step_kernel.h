@@ -150,18 +150,36 @@ struct Shape {
 };
 
 // Workgroups are handed to the eight XCDs round-robin in dispatch order
-// (block b runs on XCD b % 8).  Map block b so that each XCD walks one
-// contiguous range of (head, tile) pairs in order: the tiles of a head run
-// back to back on the same XCD (the later ones read the head's key-side log
-// from that XCD's L2), and each L2 gathers whole contiguous lines of the
-// outputs and log entries it writes instead of every eighth head's pieces.
+// (block b runs on XCD b % 8).  With XCD set, block b is mapped so that each
+// XCD walks one contiguous range of (head, tile) pairs in order, so each L2
+// gathers whole contiguous lines of the outputs and log entries it writes
+// instead of every eighth head's pieces.  Without it, block b is pair b and
+// the chip sweeps the heads in order, all eight XCDs on neighbouring heads.
+// Which is faster depends on the kernel, measured on MI355X (bench.py, back
+// to back and cold): the contiguous ranges for the single-token kernels on
+// 64 KB heads (GDN C=8 52.3 against 55.7 us/token, KDA 55.5 against 57.2);
+// the dispatch order for 16 KB heads (RWKV6 C=8 15.5 against 16.4, a read of
+// every 16 KB head 8.2 against 10.1 us) and for the multi-token kernel (GDN
+// eight tokens per call 13.1 against 13.6 us/token, KDA 13.3 against 14.1,
+// RWKV6 4.6 against 4.9).
+template <bool XCD>
 __device__ __forceinline__ void block_to_tile(int b, int N, int ntile, int &n, int &tile) {
-    const int nb = N * ntile;
-    const int x = b & 7, k = b >> 3;
-    const int g = x * (nb >> 3) + min(x, nb & 7) + k;  // XCD x owns pairs [off_x, off_x + count_x)
+    int g = b;
+    if (XCD) {
+        const int nb = N * ntile;
+        const int x = b & 7, k = b >> 3;
+        g = x * (nb >> 3) + min(x, nb & 7) + k;  // XCD x owns pairs [off_x, off_x + count_x)
+    }
     n = g / ntile;
     tile = g - n * ntile;
 }
+
+// The single-token kernels (and the probes that bound them) map 64 KB heads
+// in contiguous ranges per XCD and smaller heads in dispatch order.
+template <int DK, int DV>
+struct StepOrder {
+    static constexpr bool XCD = DK * DV >= 128 * 128;
+};
 
 // Lane exchanges that stay in the VALU (no LDS round trip): DPP moves within
 // rows of 16 lanes and the gfx950 permlane swaps across rows.
@@ -271,7 +289,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
     int n, tile;
-    block_to_tile(blockIdx.x, p.N, PREP ? 1 : NTILE, n, tile);
+    block_to_tile<StepOrder<DK, DV>::XCD>(blockIdx.x, p.N, PREP ? 1 : NTILE, n, tile);
     const int C = p.C;
     int L = LOGGED ? p.L : 0;
     if (LOGGED && p.slot_base != nullptr) {

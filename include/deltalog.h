@@ -219,6 +219,25 @@ int dl_log_length(const dl_state *h);
 size_t dl_prep_bytes(const dl_config *cfg);
 dl_status dl_set_split_replay(dl_state *h, void *prep, size_t prep_bytes);
 
+/* The decode step for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Does what dl_decode_step does in the split-replay form (see
+ * dl_set_split_replay), with the per-head prep records held in a static
+ * device array of the library -- DL_NOALLOC_PREP_BYTES (8 MiB) on each GPU
+ * it runs on, for the life of the process -- instead of a caller buffer.
+ * It allocates nothing and calls no allocating routine; the caller still
+ * passes the inputs and the output.  The first call on a device looks up
+ * that device's copy of the array (hipGetSymbolAddress).  Every call writes
+ * the records it reads and nothing carries from one call to the next; all
+ * calls on one GPU share the array, so calls that may run at the same time
+ * on one GPU (different streams, different threads) race.  Lockstep handles
+ * only (DL_ERR_UNSUPPORTED on a per-slot handle); DL_ERR_WORKSPACE when
+ * dl_prep_bytes(cfg) exceeds DL_NOALLOC_PREP_BYTES (at dk = 128 and C <= 8,
+ * for instance, up to 7598 heads); DL_ERR_HIP if the array's address cannot
+ * be found.  Otherwise as dl_decode_step. */
+#define DL_NOALLOC_PREP_BYTES (8u << 20)
+dl_status dl_decode_step_noalloc(dl_state *h, const dl_step_args *args, void *stream);
+
 /* Graph replay of one merge cycle (the pages time their kernels under graph
  * replay: signal-papers summary, Fig. 9).
  *

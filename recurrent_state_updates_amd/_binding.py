@@ -20,6 +20,7 @@ DL_ERR_ARG, DL_ERR_SHAPE, DL_ERR_UNSUPPORTED, DL_ERR_HIP, DL_ERR_WORKSPACE = -1,
 DL_MAX_CAPACITY = 32
 DL_MAX_TOKENS = 8
 DL_MAX_HEADS = 1 << 23
+DL_NOALLOC_PREP_BYTES = 8 << 20
 
 OP_CODES = {"gdn": DL_GDN, "kda": DL_KDA, "rwkv6": DL_RWKV6}
 DTYPE_CODES = {"f32": DL_F32, "bf16": DL_BF16}
@@ -69,6 +70,7 @@ def load_library():
         "dl_workspace_layout": (i, [cp, ctypes.POINTER(sz)]),
         "dl_state_init": (i, [ctypes.POINTER(vp), cp, vp, vp, sz]),
         "dl_decode_step": (i, [vp, ap, vp]),
+        "dl_decode_step_noalloc": (i, [vp, ap, vp]),
         "dl_decode_tokens": (i, [vp, ap, i, vp]),
         "dl_merge": (i, [vp, vp]),
         "dl_materialize": (i, [vp, vp, vp]),
@@ -177,6 +179,10 @@ def dl_slot_merge(handle, slot, stream=0):
 
 def dl_decode_step(handle, args, stream=0):
     _check(load_library().dl_decode_step(handle, ctypes.byref(args), stream))
+
+
+def dl_decode_step_noalloc(handle, args, stream=0):
+    _check(load_library().dl_decode_step_noalloc(handle, ctypes.byref(args), stream))
 
 
 def dl_decode_tokens(handle, args_list, stream=0):

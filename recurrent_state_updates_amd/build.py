@@ -25,10 +25,11 @@ ARCH = "gfx950"
 # compiler prints no resource remarks for them.
 OPS = {0: "gdn", 1: "kda", 2: "rwkv6"}
 KEY_WIDTHS = (32, 64, 128)
-SOURCES = [("deltalog.cpp", "deltalog", []), ("slots.hip", "slots", []), ("probe.hip", "probe", [])] + [
+SOURCES = [("deltalog.cpp", "deltalog", []), ("slots.hip", "slots", []), ("probe.hip", "probe", []),
+           ("static_prep.hip", "static_prep", [])] + [
     (f"kernels_{kind}.hip", f"kernels_{kind}_{OPS[op]}_dk{dk}", [f"-DDLK_OP={op}", f"-DDLK_DK={dk}"])
     for kind in ("step", "chunk") for op in OPS for dk in KEY_WIDTHS]
-NO_KERNELS = set()
+NO_KERNELS = {"static_prep"}
 
 # Packed fp32 VALU ops are switched off for all device code; the host pass
 # prints that it does not know the feature, which is harmless.  Matrix-core

@@ -444,6 +444,42 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *a, void *stream) {
     return DL_OK;
 }
 
+dl_status dl_decode_step_noalloc(dl_state *h, const dl_step_args *a, void *stream) {
+    if (!h) return fail(DL_ERR_ARG, "handle is NULL");
+    if (h->slots) return fail(DL_ERR_UNSUPPORTED, "the allocation-free decode step needs a lockstep handle");
+    size_t heads = 0;
+    dl_status st = check_config(&h->cfg, &heads);
+    if (st != DL_OK) return st;
+    const size_t need = dl_prep_bytes(&h->cfg);
+    if (need > DL_NOALLOC_PREP_BYTES)
+        return fail(DL_ERR_WORKSPACE, "this configuration's prep records take " + std::to_string(need) +
+                                          " bytes, more than the static scratch of DL_NOALLOC_PREP_BYTES = " +
+                                          std::to_string((size_t)DL_NOALLOC_PREP_BYTES));
+    st = check_step(h, a);
+    if (st != DL_OK) return st;
+    dlk::StepParams p = params_of(&h->cfg, heads);
+    set_log(p, h);
+    set_token(p, a);
+    p.dst = h->base;
+    const bool fold = h->L + 1 == h->cfg.C;
+    if (fold) {
+        // the fold step keeps its fused form (as with a prep buffer): no scratch
+        p.prep = nullptr;
+        st = launch(&h->cfg, dlk::MODE_MERGE, p, stream);
+    } else {
+        void *scr = nullptr;
+        const hipError_t e = dlk::static_prep_scratch(&scr);
+        if (e != hipSuccess)
+            return fail(DL_ERR_HIP, std::string("static scratch lookup failed: ") + hipGetErrorString(e));
+        p.prep = static_cast<float *>(scr);
+        st = launch(&h->cfg, dlk::MODE_PREP, p, stream);
+        if (st == DL_OK) st = launch(&h->cfg, dlk::MODE_PREPPED, p, stream);
+    }
+    if (st != DL_OK) return st;
+    h->L = fold ? 0 : h->L + 1;
+    return DL_OK;
+}
+
 dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *stream) {
     if (!h) return fail(DL_ERR_ARG, "handle is NULL");
     size_t heads = 0;

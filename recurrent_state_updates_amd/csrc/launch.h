@@ -97,6 +97,11 @@ struct ChunkParams {
 template <int OP, int DK>
 hipError_t launch_chunk(int in_bf16, int DV, int cmax, const ChunkParams &p, hipStream_t s);
 
+// The device address of this GPU's copy of the allocation-free decode
+// step's scratch (DL_NOALLOC_PREP_BYTES bytes; static_prep.hip), looked up
+// once per device with that device current.
+hipError_t static_prep_scratch(void **ptr);
+
 // Set slot_base / slot_active entries: slot < 0 means every slot (with
 // only_active, every active slot); set_base / set_active select the fields.
 hipError_t launch_slot_set(int *slot_base, unsigned char *slot_active, int B, int slot, int set_base,

@@ -110,6 +110,16 @@ class DeltaLogState:
         B.dl_decode_step(self.handle, args, _stream(self.device))
         return out
 
+    def step_noalloc(self, q, k, v, beta, decay, bonus=None, out=None):
+        """dl_decode_step_noalloc: one token in the split-replay form with the
+        library's static scratch (no prep buffer of this handle is used)."""
+        if out is None:
+            out = torch.empty((self.B, self.H, self.dv), dtype=torch.float32, device=self.device)
+        args = make_step_args(self.op, self.in_dtype, self.B, self.H, self.dk, self.dv,
+                              self.device, q, k, v, beta, decay, bonus, out)
+        B.dl_decode_step_noalloc(self.handle, args, _stream(self.device))
+        return out
+
     def step_tokens(self, q, k, v, beta, decay, bonus=None, out=None):
         """Decode K tokens in one call (dl_decode_tokens).  q, k, v, beta, decay
         carry a leading token axis [K, ...]; returns out [K, B, H, dv] fp32."""

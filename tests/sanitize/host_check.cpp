@@ -124,6 +124,15 @@ static void check_lockstep(int op, int dk, int dv) {
     }
     CHECK(g_launches.back().mode == dlk::MODE_MERGE);
     CHECK(dl_set_split_replay(h, nullptr, 0) == DL_OK);
+    // the allocation-free step: the same two stages on the static scratch, the fold fused
+    g_launches.clear();
+    for (int t = 0; t < C; ++t) CHECK(dl_decode_step_noalloc(h, &a0, nullptr) == DL_OK);
+    CHECK(g_launches.size() == (size_t)2 * (C - 1) + 1);
+    for (int t = 0; t < C - 1; ++t) {
+        CHECK(g_launches[2 * t].mode == dlk::MODE_PREP && g_launches[2 * t].prep && g_launches[2 * t].L == t);
+        CHECK(g_launches[2 * t + 1].mode == dlk::MODE_PREPPED && g_launches[2 * t + 1].prep);
+    }
+    CHECK(g_launches.back().mode == dlk::MODE_MERGE && !g_launches.back().prep && dl_log_length(h) == 0);
     // several tokens per call: within the log, filling it, passing its end, and one token
     std::vector<dl_step_args> toks;
     for (int t = 0; t < 8; ++t) toks.push_back(token(op, t));
@@ -233,12 +242,36 @@ static void check_slots(int op) {
     for (int b = 0; b < B; ++b)
         if (b != 3) CHECK(dl_slot_log_length(h, b) == 0);
     CHECK(dl_set_split_replay(h, addr(PREP), dl_prep_bytes(&c)) == DL_ERR_UNSUPPORTED);
+    CHECK(dl_decode_step_noalloc(h, &a, nullptr) == DL_ERR_UNSUPPORTED);
     CHECK(dl_log_length(h) == -1);
     dl_state_destroy(h);
 }
 
+// The allocation-free step refuses a configuration whose records exceed its scratch.
+static void check_noalloc_limit() {
+    for (int heads : {7598, 7599}) {
+        dl_config c = {DL_GDN, DL_BF16, heads, 1, 128, 128, 8};
+        CHECK(dl_prep_bytes(&c) == (size_t)heads * 1104);
+        dl_state *h = nullptr;
+        CHECK(dl_state_init(&h, &c, static_cast<float *>(addr(BASE)), addr(BASE + (1ull << 36)),
+                            dl_workspace_bytes(&c)) == DL_OK);
+        dl_step_args a = token(DL_GDN, 0);
+        a.q = addr(BASE + (2ull << 36));  // inputs clear of this large base
+        a.k = addr(BASE + (2ull << 36) + (1ull << 30));
+        a.v = addr(BASE + (2ull << 36) + (2ull << 30));
+        a.beta = static_cast<const float *>(addr(BASE + (2ull << 36) + (3ull << 30)));
+        a.decay = static_cast<const float *>(addr(BASE + (2ull << 36) + (4ull << 30)));
+        a.out = static_cast<float *>(addr(BASE + (2ull << 36) + (5ull << 30)));
+        const int rc = dl_decode_step_noalloc(h, &a, nullptr);
+        CHECK(rc == (heads == 7598 ? DL_OK : DL_ERR_WORKSPACE));
+        CHECK(dl_log_length(h) == (heads == 7598 ? 1 : 0));
+        dl_state_destroy(h);
+    }
+}
+
 int main() {
     check_configs();
+    check_noalloc_limit();
     for (int op = 0; op < 3; ++op) {
         check_lockstep(op, 128, 128);
         check_lockstep(op, 64, 128);

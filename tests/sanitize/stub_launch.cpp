@@ -5,6 +5,8 @@
 // behaviour sanitizers) on a machine without a GPU.  Test infrastructure.
 #include "stub_launch.h"
 
+#include <stdint.h>
+
 namespace dlk {
 
 std::vector<Launch> g_launches;
@@ -36,6 +38,12 @@ hipError_t launch_slot_set(int *, unsigned char *, int B, int slot, int set_base
     l.B = B, l.slot = slot, l.set_base = set_base, l.base_value = base_value, l.set_active = set_active;
     l.active_value = active_value, l.only_active = only_active;
     g_launches.push_back(l);
+    return hipSuccess;
+}
+
+// A fake address standing for the static scratch of dl_decode_step_noalloc.
+hipError_t static_prep_scratch(void **ptr) {
+    *ptr = reinterpret_cast<void *>(static_cast<uintptr_t>(0x7e0000000000ull));
     return hipSuccess;
 }
 

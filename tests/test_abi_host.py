@@ -46,7 +46,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     for name in names:
         assert hasattr(lib, name), f"{name} is declared in deltalog.h but not exported"
     for name in names:
@@ -367,3 +367,26 @@ def test_probe_validates_on_the_host():
     assert lib.dl_probe_stream(1, FAKE, 1 << 22, 4, 64, 64, sink, None) == -2    # too many heads
     assert lib.dl_probe_stream(0, FAKE, 1, 1, 64, 48, sink, None) == -3          # width not built
     assert "32, 64 or 128" in lib.dl_probe_last_error().decode()
+
+
+def test_noalloc_step_validates_on_the_host():
+    lib = B.load_library()
+    assert lib.dl_decode_step_noalloc(None, ctypes.byref(_args()), None) == B.DL_ERR_ARG
+    # a configuration whose prep records exceed the static scratch is refused before anything runs
+    big = dl.make_config("gdn", "bf16", 2048, 4, 128, 128, 8)  # 8192 heads x 1104 B > 8 MiB
+    assert dl.dl_prep_bytes(big) > B.DL_NOALLOC_PREP_BYTES
+    h = dl.dl_state_init(big, FAKE + (1 << 36), FAKE + (1 << 37), dl.dl_workspace_bytes(big))
+    try:
+        assert lib.dl_decode_step_noalloc(h, ctypes.byref(_args()), None) == B.DL_ERR_WORKSPACE
+        assert "DL_NOALLOC_PREP_BYTES" in dl.dl_last_error()
+        assert dl.dl_log_length(h) == 0
+    finally:
+        dl.dl_state_destroy(h)
+    cfg = dl.make_config("kda", "bf16", 2, 4, 64, 64, 4)
+    h = dl.dl_state_init(cfg, FAKE, WS, dl.dl_workspace_bytes(cfg))
+    try:
+        assert lib.dl_decode_step_noalloc(h, ctypes.byref(_args(k=0)), None) == B.DL_ERR_ARG
+        assert lib.dl_decode_step_noalloc(h, ctypes.byref(_args(out=WS + 0x100)), None) == B.DL_ERR_ARG
+        assert dl.dl_log_length(h) == 0
+    finally:
+        dl.dl_state_destroy(h)

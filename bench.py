@@ -359,14 +359,19 @@ def main():
         cold = cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, args.tokens, flush)
         cold["frac_of_peak"] = round(cold["achieved_GBps"] / PEAK_HBM_GBPS, 4)
         cold["isolated"]["frac_of_peak"] = round(cold["isolated"]["achieved_GBps"] / PEAK_HBM_GBPS, 4)
+        # fractions of the ceilings are rates: the kernel's algorithmic bytes per
+        # microsecond over the probe's (the append also moves its tokens and log)
         if C > 1:
             app_cold = float(np.mean(cold["append_by_L"]))
             cold["append_mean_us"] = round(app_cold, 2)
-            cold["append_frac_of_read_ceiling"] = round(ceil["read"]["cold_us"] / app_cold, 4)
-        cold["decode_fold_frac_of_copy_ceiling"] = round(ceil["copy"]["cold_us"] / cold["decode_fold"], 4)
+            cold["append_frac_of_read_ceiling"] = round(
+                (dom_bytes / app_cold) / (ceil["read"]["bytes"] / ceil["read"]["cold_us"]), 4)
+        cold["decode_fold_frac_of_copy_ceiling"] = round(
+            (traffic.merge_bytes(sh, C) / cold["decode_fold"]) / (ceil["copy"]["bytes"] / ceil["copy"]["cold_us"]), 4)
         result["cold"] = cold
         if C > 1:
-            result["roofline"]["frac_of_read_ceiling"] = round(ceil["read"]["warm_us"] / dom_us, 4)
+            result["roofline"]["frac_of_read_ceiling"] = round(
+                (dom_bytes / dom_us) / (ceil["read"]["bytes"] / ceil["read"]["warm_us"]), 4)
         del flush
 
     if args.capacity_study and not args.no_cold:

@@ -319,11 +319,12 @@ dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *
  * read_gbps; the token that fills the log moves the base twice, at copy_gbps
  * (gist.science summary, "Modello di Traffico": appends of compact factors,
  * one amortised dense write per interval, replay of the log).  Bandwidths
- * <= 0 select the values fitted to these kernels' measured times on MI355X
- * (6250 GB/s for appends, 5675 GB/s for the fold; within 2 % of the measured
- * amortised time for C = 1..32 at GDN and KDA B=128 d=128, launch gaps
- * included).  Host-only.  Returns a negative value for an
- * invalid cfg. */
+ * <= 0 select the stream ceilings measured on MI355X at the kernels' own
+ * access pattern (include/deltalog_probe.h), in sequence with a cold
+ * Infinity Cache: 6760 GB/s for a read of every head, 5580 GB/s for an
+ * in-place copy.  The kernels run at 85-96 % of those ceilings, so the
+ * prediction is a lower bound, 5-15 % under the measured time.  Host-only.
+ * Returns a negative value for an invalid cfg. */
 double dl_predict_token_us(const dl_config *cfg, double read_gbps, double copy_gbps);
 
 /* The capacity C in [1, max_c] (max_c <= DL_MAX_CAPACITY) with the smallest

@@ -779,8 +779,11 @@ dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *
 double dl_predict_token_us(const dl_config *cfg, double read_gbps, double copy_gbps) {
     size_t heads = 0;
     if (check_config(cfg, &heads) != DL_OK) return -1.0;
-    if (read_gbps <= 0) read_gbps = 6250.0;
-    if (copy_gbps <= 0) copy_gbps = 5675.0;
+    // defaults: the stream ceilings of the kernels' own access pattern on
+    // MI355X, measured in sequence with a cold Infinity Cache (bench.py's
+    // `ceilings`, GDN B=128 H=32 d=128): a read of every head, an in-place copy
+    if (read_gbps <= 0) read_gbps = 6760.0;
+    if (copy_gbps <= 0) copy_gbps = 5580.0;
     const HeadBytes b = head_bytes(cfg);
     const double n = (double)heads;
     const int C = cfg->C;

@@ -7,10 +7,13 @@
 // log for each, and resolves the dependence of token t on the earlier tokens
 // of the chunk by a forward substitution over the value factors, column by
 // column.  The tokens are then appended to the log, or, when the chunk fills
-// it, the whole log is folded into the base with one read and one write.  If
-// the log fills before the call's last token (on a per-slot handle, at each
-// slot's own token), the fold leaves the new base in the registers and the
-// rest of the tokens run as a further segment on an empty log.
+// it, the log's first C entries are folded into the base with one read and
+// one write and the tokens past the fold start the new log.  All the tokens'
+// products are taken from the base as read (the fold is exact algebra, so a
+// token after it sees the same state either way).  A call of more tokens than
+// C folds more than once; there (SEG) the fold leaves the new base in the
+// registers and the rest of the tokens run as a further segment on an empty
+// log.
 //
 // Algebra (per head; g_t = g_L + sum_{m<=t} log2 decay_m, g_{-1} = g_L; the
 // reference point rho_t = g_t for the delta rules, g_{t-1} for RWKV6):
@@ -19,8 +22,10 @@
 //   delta rules    u_t = beta_t (v_t - Y0_t - sum_{m<t} u_m <k_m 2^{g_t-g_m}, k_t>)
 //                  o_t = Z0_t + sum_{m<t} u_m <k_m 2^{g_t-g_m}, q_t> + <k_t, q_t> u_t
 //   RWKV6          o_t = Z0_t + sum_{m<t} v_m <k_m 2^{g_{t-1}-g_m}, r_t> + (sum_c r u k) v_t
-//   entries        (k_t, u_t or v_t, g_t); a fold writes
-//                  S = diag(2^{g_{K-1}}) Sbar + sum_e (k_e 2^{g_{K-1}-g_e}) x_e^T over all entries.
+//   entries        (k_t, u_t or v_t, g_t); when the log fills at token f = C-1-L a fold writes
+//                  S = diag(2^{g_f}) Sbar + sum_{e<C} (k_e 2^{g_f-g_e}) x_e^T,
+//                  and the tokens t > f become entries t-f-1 of the new log with
+//                  their log-decays summed from the fold: g'_t = sum_{f<m<=t} log2 decay_m.
 #pragma once
 
 #include "step_kernel.h"
@@ -32,6 +37,21 @@ __device__ __forceinline__ void store_raw(float *dst, float x) { *dst = x; }
 __device__ __forceinline__ void store_raw(bf16_bits *dst, float x) {
     *dst = static_cast<bf16_bits>(__float_as_uint(x) >> 16);
 }
+
+// The same for four consecutive values: the inverse of In4<TIn>::unpack.
+template <typename TIn>
+struct Pack4;
+template <>
+struct Pack4<float> {
+    __device__ static f4 pack(f4 x) { return x; }
+};
+template <>
+struct Pack4<bf16_bits> {
+    __device__ static u2 pack(f4 x) {
+        return u2{(__float_as_uint(x.x) >> 16) | (__float_as_uint(x.y) & 0xffff0000u),
+                  (__float_as_uint(x.z) >> 16) | (__float_as_uint(x.w) & 0xffff0000u)};
+    }
+};
 
 // Token pointers of the kernel arguments as opaque scalar values.  The lanes
 // of one wave belong to GPW consecutive key-side groups (tokens tb + t0 ..
@@ -66,13 +86,12 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
 // each 16x16x4 k-step is four rows of one half and two waves' products add up
 // per column.  The vector form (every other shape) holds whole heads as row
 // passes.
-// SEG runs every segment of the call in one workgroup: when the log fills
-// before the call's last token, the fold updates the register tile in place
-// and the rest of the tokens start an empty log from it (per-slot handles,
-// and calls that pass C).  Without SEG the chunk fits the log.  The
-// segmented matrix-core form at C <= 8 asks for three waves per SIMD, which
-// the compiler meets without spilling (left alone, KDA settles one register
-// above that, at two waves).
+// Without SEG the call folds at most once (K <= C), at each workgroup's own
+// token on a per-slot handle.  SEG runs calls of more tokens than C (C < 8)
+// as segments in one workgroup: each fold updates the register tile in place
+// and the next tokens start an empty log from it.  The segmented matrix-core
+// form asks for three waves per SIMD, which the compiler meets without
+// spilling (left alone, KDA settles one register above that, at two waves).
 template <int OP, typename TIn, int DK, int DV, int TV, int NT, int CMAX, bool MM, bool SEG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SEG && MM && CMAX == 8 ? 3 : 1)))
 void chunk_kernel(const ChunkParams p) {
@@ -82,8 +101,11 @@ void chunk_kernel(const ChunkParams p) {
     constexpr bool GDN = OP == OP_GDN;
     constexpr bool DELTA = OP != OP_RWKV6;
     constexpr int KM = KMAX_TOKENS;
-    constexpr int CP = CMAX;  // entry slots: old entries plus the chunk's tokens (<= C <= CMAX)
-    constexpr int KPASS = (CMAX + EPP - 1) / EPP;
+    // entry slots: the old entries and the chunk's tokens (L + K <= C - 1 + KM
+    // without SEG; a segment never passes C)
+    constexpr int CP = SEG ? CMAX : CMAX + KM;
+    constexpr int KPASS_OLD = (CMAX + EPP - 1) / EPP;  // key-side passes over the old entries (L < C)
+    constexpr int KPASS = (CP + EPP - 1) / EPP;         // ... over every entry slot
     static_assert(!MM || (DK == 128 && DV == 128 && TV == DV && NT == 256 && 2 * KM == 16),
                   "matrix-core form: whole 128 x 128 heads, 256 threads, 16 product vectors");
     // s[i] holds tile row rbase + RSTEP * i; xrow[j] holds log entry ebase + ESTEP * j
@@ -98,7 +120,8 @@ void chunk_kernel(const ChunkParams p) {
     static_assert(KM <= EPP, "one key-side group per token");
     static_assert(64 % KL == 0, "key-side groups do not straddle waves");
     static_assert(R % 4 == 0, "a thread's rows of the scaled vectors are read as float4");
-    static_assert(CMAX % 4 == 0, "entry slots come in groups of four");
+    static_assert(CMAX % 4 == 0 && CP % 4 == 0, "entry slots come in groups of four");
+    static_assert(!SEG || CMAX == 8, "segmented calls have C < KMAX_TOKENS");
 
     // LDS.  Phase B's token-side arrays (keys, queries, log-decays, the scaled
     // vectors) are dead once phase C has read its operands, so in the
@@ -126,14 +149,14 @@ void chunk_kernel(const ChunkParams p) {
     auto &s_lg = *reinterpret_cast<float (*)[KM][GW]>(s_pool + 3 * SZ_K + SZ_MV0);  // log2 of each token's decay
     auto &s_g = *reinterpret_cast<float (*)[KM + 1][GW]>(s_pool + 3 * SZ_K + SZ_MV0 + SZ_LG);  // g_{t-1} at index t (g_{-1} = g_L)
     auto &s_red = *reinterpret_cast<float (*)[KM][NWR][NS][TV]>(s_pool + (MM ? 0 : SZ_B));
-    __shared__ __attribute__((aligned(16))) float s_scale[DK];     // fold: 2^{g_{K-1}} per row
-    __shared__ __attribute__((aligned(16))) float s_kt[CP * DK];   // fold: decayed keys [entry][row]
-    // value factors [entry][col] for the fold.  In the matrix-core form rows
-    // L .. L+K-1 first hold the chunk's values (phase D reads v_t there and
-    // writes u_t in its place), and row CP takes the writes of token slots past
-    // the chunk.
-    __shared__ __attribute__((aligned(16))) float s_x[(CP + (MM ? 1 : 0)) * TV];
-    __shared__ float s_coef[2][KM][CP];                            // per token, per entry
+    __shared__ __attribute__((aligned(16))) float s_scale[DK];     // fold: 2^{g_f} per row
+    __shared__ __attribute__((aligned(16))) float s_kt[CMAX * DK]; // fold: decayed keys [entry][row], entries < C
+    // value factors [entry][col] for the fold (entries < C).  In the
+    // matrix-core form rows L .. L+K-1 first hold the chunk's values (phase D
+    // reads v_t there and writes u_t in its place, or sends it to the new log
+    // past the fold), and row CP takes the writes of token slots past the chunk.
+    __shared__ __attribute__((aligned(16))) float s_x[(MM ? CP + 1 : CMAX) * TV];
+    __shared__ float s_coef[NS][KM][CP];  // per side (keys, queries), token and entry
     __shared__ float s_dot[KM];   // <k_t, q_t> or sum r u k
     __shared__ float s_beta[KM + 1];  // slot KM takes the writes of lanes that hold no token
 
@@ -156,8 +179,9 @@ void chunk_kernel(const ChunkParams p) {
     }
     // with SEG the first segment runs up to the fold (or the call's end)
     int K = SEG ? min(p.K, C - L) : p.K;
-    bool fold = SEG ? L + K == C : p.fold != 0;
+    bool fold = L + K >= C;
     int NE = L + K;                     // entries after the segment
+    int tf = fold ? C - 1 - L : K - 1;  // the token at which the log fills
     const int last = L > 0 ? L - 1 : 0;
     // the thread's rows of the tile, its four columns (from cq, within the
     // tile) and its rows of the old log's value factors
@@ -280,21 +304,33 @@ void chunk_kernel(const ChunkParams p) {
             }
         }
         __syncthreads();
-        // prefix sums of the log-decays: g_t for every token (group 0, four channels per thread)
+        // prefix sums of the log-decays: g_t for every token (group 0, four
+        // channels per thread); a token past the fold also gets g'_t, its sum
+        // from the fold, in place of its own log-decay
         if (ke == 0) {
             if (GDN) {
                 if (c4 == 0) {
-                    float g = s_g[0][0];
+                    float g = s_g[0][0], g2 = 0.f;
                     for (int t = 0; t < K; ++t) {
-                        g += s_lg[t][0];
+                        const float lg = s_lg[t][0];
+                        g += lg;
                         s_g[t + 1][0] = g;
+                        if (!SEG && t > tf) {
+                            g2 += lg;
+                            s_lg[t][0] = g2;
+                        }
                     }
                 }
             } else {
-                f4 g = *reinterpret_cast<const f4 *>(&s_g[0][c4]);
+                f4 g = *reinterpret_cast<const f4 *>(&s_g[0][c4]), g2 = {0.f, 0.f, 0.f, 0.f};
                 for (int t = 0; t < K; ++t) {
-                    g += *reinterpret_cast<const f4 *>(&s_lg[t][c4]);
+                    const f4 lg = *reinterpret_cast<const f4 *>(&s_lg[t][c4]);
+                    g += lg;
                     *reinterpret_cast<f4 *>(&s_g[t + 1][c4]) = g;
+                    if (!SEG && t > tf) {
+                        g2 += lg;
+                        *reinterpret_cast<f4 *>(&s_lg[t][c4]) = g2;
+                    }
                 }
             }
         }
@@ -341,19 +377,21 @@ void chunk_kernel(const ChunkParams p) {
                 }
             }
         }
-        if (fold && ke == 0) *reinterpret_cast<f4 *>(&s_scale[c4]) = exp2v(g_at(K));
+        if (fold && ke == 0) *reinterpret_cast<f4 *>(&s_scale[c4]) = exp2v(g_at(SEG ? K : tf + 1));
 
         // ---------------- Phase B3: coefficients of every (token, entry) pair ----------------
-        const f4 gend = g_at(K);  // g_{K-1}: the fold's decay point
+        const f4 gend = g_at(SEG ? K : tf + 1);  // g_f: the fold's decay point
 #pragma unroll
         for (int ps = 0; ps < KPASS; ++ps) {
+            if (ps > 0 && ps * EPP >= NE) break;
             const int e = ps * EPP + ke;
-            const bool is_old = FIRST && e < L;
+            const int po = ps < KPASS_OLD ? ps : KPASS_OLD - 1;
+            const bool is_old = FIRST && ps < KPASS_OLD && e < L;
             const bool is_new = e >= L && e < NE;
             f4 ke4, ge4;
             if (is_old) {
-                ke4 = In4<TIn>::unpack(klog[ps]);
-                ge4 = GDN ? f4{glog_s[ps], glog_s[ps], glog_s[ps], glog_s[ps]} : glog4[ps];
+                ke4 = In4<TIn>::unpack(klog[po]);
+                ge4 = GDN ? f4{glog_s[po], glog_s[po], glog_s[po], glog_s[po]} : glog4[po];
             } else if (is_new) {
                 ke4 = *reinterpret_cast<const f4 *>(&s_k[e - L][c4]);
                 ge4 = g_at(e - L + 1);
@@ -391,30 +429,52 @@ void chunk_kernel(const ChunkParams p) {
                 for (int t = 0; t < KM; ++t) {
                     if (t < K) {
                         if (DELTA) s_coef[0][t][e] = pk[t];
-                        s_coef[1][t][e] = pq[t];
+                        s_coef[ZS][t][e] = pq[t];
                     }
                 }
             }
-            if (fold && (is_old || is_new))
+            if (fold && (is_old || is_new) && (SEG || e < C))
                 *reinterpret_cast<f4 *>(&s_kt[e * DK + c4]) = ke4 * exp2v(gend - ge4);
         }
+        if constexpr (!SEG) {
+            // The tokens past a fold start the new log: group j writes entry j,
+            // token f + 1 + j's key copy (its input bits, from the exact fp32
+            // copy) and g'_j.  Slot j is the one whose old entry this same group
+            // read in phase A (or a slot no group read), and the group has used
+            // that entry above, so the write cannot overtake the read.
+            const int t = tf + 1 + ke;
+            if (fold && t < K && tile == 0) {
+                const size_t e = (size_t)n * C + ke;
+                *reinterpret_cast<Raw *>(static_cast<TIn *>(p.logK) + e * DK + c4) =
+                    Pack4<TIn>::pack(*reinterpret_cast<const f4 *>(&s_k[t][c4]));
+                if (GDN) {
+                    if (c4 == 0) p.logG[e] = s_lg[t][0];
+                } else {
+                    *reinterpret_cast<f4 *>(p.logG + e * DK + c4) = *reinterpret_cast<const f4 *>(&s_lg[t][c4]);
+                }
+            }
+        }
         if (fold) {
-            // old value factors of the tile for the fold; zero the slots up to a multiple of four
+            // old value factors of the tile for the fold; zero the fold's entry
+            // slots from C up to a multiple of four (without SEG the
+            // matrix-core form keeps token values in those rows of s_x and
+            // masks them in the fold)
 #pragma unroll
             for (int j = 0; j < XR; ++j) {
                 const int i = ebase + ESTEP * j;
                 if (FIRST && i < L) *reinterpret_cast<f4 *>(&s_x[i * TV + cq]) = In4<TX>::unpack(xrow[j]);
             }
             constexpr int W = DK > TV ? DK : TV;
-            const int pad = ((NE + 3) & ~3) - NE;
+            const int pad = ((C + 3) & ~3) - C;
             for (int idx = tid; idx < pad * W; idx += NT) {
-                const int i = NE + idx / W;
+                const int i = C + idx / W;
                 const int c = idx % W;
                 if (c < DK) s_kt[i * DK + c] = 0.f;
-                if (c < TV) s_x[i * TV + c] = 0.f;
+                if ((SEG || !MM) && c < TV) s_x[i * TV + c] = 0.f;
             }
         }
         __syncthreads();
+
 
         // ---------------- Phase C: base products of every token from the register tile ----------------
         if constexpr (MM) {
@@ -457,7 +517,7 @@ void chunk_kernel(const ChunkParams p) {
                 // anything (an unused slot holds whatever the workspace held): zero
                 // both operands, since 0 * NaN would poison the sum
                 const int e = ebase + ESTEP * j;
-                const float co = (FIRST && live && e < L) ? s_coef[side][tm][e] : 0.f;
+                const float co = (FIRST && live && e < L) ? s_coef[DELTA ? side : ZS][tm][e] : 0.f;
                 const f4 xv = FIRST && e < L ? In4<TX>::unpack(xrow[j]) : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(co, xv[c], acc[c], 0, 0, 0);
@@ -491,7 +551,7 @@ void chunk_kernel(const ChunkParams p) {
                     if (FIRST && i < L) {
                         const f4 x = In4<TX>::unpack(xrow[j]);
                         if (DELTA) y += s_coef[0][t][i] * x;
-                        z += s_coef[1][t][i] * x;
+                        z += s_coef[ZS][t][i] * x;
                     }
                 }
 #pragma unroll
@@ -525,7 +585,7 @@ void chunk_kernel(const ChunkParams p) {
                 for (int m = 0; m < KM; ++m) {
                     if (m >= t) break;
                     if (DELTA) yj += s_coef[0][t][L + m] * xs[m];
-                    zj += s_coef[1][t][L + m] * xs[m];
+                    zj += s_coef[ZS][t][L + m] * xs[m];
                 }
                 const float vj = MM ? s_x[(L + t) * TV + jt] : to_f32(vraw[t]);
                 float xnew, o;
@@ -538,10 +598,13 @@ void chunk_kernel(const ChunkParams p) {
                 }
                 xs[t] = xnew;
                 p.out[tb + t][(size_t)n * DV + j] = o;
-                if (fold) {
+                const bool past = !SEG && fold && t > tf;
+                if (fold && !past) {
                     s_x[(L + t) * TV + jt] = xnew;
                 } else {
-                    const size_t e = (size_t)n * C + L + t;
+                    // the old value rows this overwrites past a fold were
+                    // consumed before phase C's barrier
+                    const size_t e = (size_t)n * C + (past ? t - tf - 1 : L + t);
                     if (DELTA)
                         static_cast<float *>(p.logX)[e * DV + j] = xnew;
                     else
@@ -550,7 +613,7 @@ void chunk_kernel(const ChunkParams p) {
             }
         }
 
-        // ---------------- Phase E: fold every entry into the base when the chunk fills the log ----------------
+        // ---------------- Phase E: fold the log's C entries into the base when the chunk fills it ----------------
         if (fold) {
             __syncthreads();
             f4 *dst4 = reinterpret_cast<f4 *>(p.base) + tile4;
@@ -562,7 +625,9 @@ void chunk_kernel(const ChunkParams p) {
                 // = the update of its own s[4 g + q][c].  Each group's rows are stored
                 // as soon as they are done, so that one group's products are live at
                 // a time.
-                // The entry slots past NE are zero up to a multiple of four.
+                // The key slots from C up to a multiple of four are zero; without
+                // SEG the value rows there may hold later tokens' values and are
+                // masked.
                 typedef float m4 __attribute__((ext_vector_type(4)));
                 const int m = lane & 15, kr = lane >> 4;
 #pragma unroll
@@ -571,9 +636,10 @@ void chunk_kernel(const ChunkParams p) {
                     m4 pc[4];
 #pragma unroll
                     for (int c = 0; c < 4; ++c) pc[c] = m4{0.f, 0.f, 0.f, 0.f};
-                    for (int e = 0; e < NE; e += 4) {
+                    for (int e = 0; e < C; e += 4) {
                         const float av = s_kt[(e + kr) * DK + arow];
-                        const f4 bv = *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + cq]);
+                        const f4 bv = SEG || e + kr < C ? *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + cq])
+                                                        : f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int c = 0; c < 4; ++c) pc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[c], pc[c], 0, 0, 0);
                     }
@@ -589,7 +655,7 @@ void chunk_kernel(const ChunkParams p) {
                 f4 acc[R];
 #pragma unroll
                 for (int i = 0; i < R; ++i) acc[i] = s[i] * s_scale[rbase + RSTEP * i];
-                for (int e = 0; e < NE; e += 4) {
+                for (int e = 0; e < C; e += 4) {
                     const f4 x0 = *reinterpret_cast<const f4 *>(&s_x[(e + 0) * TV + cq]);
                     const f4 x1 = *reinterpret_cast<const f4 *>(&s_x[(e + 1) * TV + cq]);
                     const f4 x2 = *reinterpret_cast<const f4 *>(&s_x[(e + 2) * TV + cq]);
@@ -622,6 +688,7 @@ void chunk_kernel(const ChunkParams p) {
             K = min(p.K - tb, C);
             fold = K == C;
             NE = K;
+            tf = K - 1;
             __syncthreads();  // every read of the last segment's LDS is done
             load_tokens();
             stage_tokens();
@@ -660,8 +727,10 @@ hipError_t launch_chunk_form(const ChunkParams &p, hipStream_t s) {
 
 template <int OP, typename TIn, int DK, int DV, int CMAX>
 hipError_t launch_chunk_one(const ChunkParams &p, hipStream_t s) {
-    return p.segmented ? launch_chunk_form<OP, TIn, DK, DV, CMAX, true>(p, s)
-                       : launch_chunk_form<OP, TIn, DK, DV, CMAX, false>(p, s);
+    if (!p.segmented) return launch_chunk_form<OP, TIn, DK, DV, CMAX, false>(p, s);
+    // more tokens than C: C < KMAX_TOKENS, within the smallest bound
+    if constexpr (CMAX == 8) return launch_chunk_form<OP, TIn, DK, DV, CMAX, true>(p, s);
+    return hipErrorInvalidValue;
 }
 
 template <int OP, typename TIn, int DK, int DV>

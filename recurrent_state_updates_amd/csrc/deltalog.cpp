@@ -545,10 +545,10 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
     // one token: the single-token kernel is faster than a chunk of one
     if (K == 1) return dl_decode_step(h, &args[0], stream);
     if (h->slots) {
-        // Every slot's log fills at its own token: one segmented launch, in
-        // which each slot folds when its log fills and goes on from there.
+        // Every slot's log fills at its own token: one launch, in which each
+        // slot folds when its log fills and goes on from there.
         dlk::ChunkParams p = chunk_of(0, K);
-        p.segmented = 1;
+        p.segmented = K > h->cfg.C;
         p.slot_base = h->slot_base;
         p.slot_active = h->slot_active;
         p.step = h->step;
@@ -556,14 +556,11 @@ dl_status dl_decode_tokens(dl_state *h, const dl_step_args *args, int K, void *s
         h->step += (unsigned)K;
         return DL_OK;
     }
+    // a call that passes the log's end folds there and goes on in the same
+    // launch; one of more tokens than C folds more than once (segmented)
     dlk::ChunkParams p = chunk_of(0, K);
     p.L = h->L;
-    if (h->L + K > h->cfg.C) {
-        // the call passes the log's end: fold there and go on in the same launch
-        p.segmented = 1;
-    } else {
-        p.fold = h->L + K == h->cfg.C;
-    }
+    p.segmented = K > h->cfg.C;
     if ((st = launch_chunk(p)) != DL_OK) return st;
     h->L = (h->L + K) % h->cfg.C;
     return DL_OK;

@@ -76,16 +76,17 @@ struct ChunkParams {
     void *logX;
     void *logK;
     float *logG;
-    int L;     // log entries before the chunk
-    int C;     // capacity; L + K <= C
+    int L;     // log entries before the chunk, L < C
+    int C;     // capacity
     int H;
     int N;
     int K;     // tokens in the chunk, 1 <= K <= KMAX_TOKENS
-    int fold;  // 1: L + K == C, fold every entry into the base
-    // segmented != 0: the K tokens may pass the log's end; the kernel folds
-    // when the log fills and starts an empty log for the rest (fold is then
-    // ignored).  Per-slot handles (slot_base != NULL) are always segmented:
-    // each slot's log length is (step - slot_base[b]) mod C, and L is ignored.
+    // The kernel folds the log's first C entries into the base when L + K >= C
+    // and starts the new log with the tokens past the fold.  segmented == 0
+    // requires K <= C (at most one fold per call); segmented != 0 (K > C, so
+    // C < KMAX_TOKENS) folds each time the log fills.  On per-slot handles
+    // (slot_base != NULL) each slot's log length is (step - slot_base[b]) mod C,
+    // and L is ignored.
     int segmented;
     const int *slot_base;
     const unsigned char *slot_active;

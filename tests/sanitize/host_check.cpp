@@ -139,13 +139,16 @@ static void check_lockstep(int op, int dk, int dv) {
     g_launches.clear();
     CHECK(dl_decode_tokens(h, toks.data(), 3, nullptr) == DL_OK);  // L 0 -> 3
     CHECK(g_launches.back().kind == dlk::KIND_CHUNK && g_launches.back().L == 0 && g_launches.back().K == 3);
-    CHECK(!g_launches.back().fold && !g_launches.back().segmented && dl_log_length(h) == 3);
+    CHECK(!g_launches.back().segmented && dl_log_length(h) == 3);
     CHECK(dl_decode_tokens(h, toks.data(), 2, nullptr) == DL_OK);  // L 3 -> fills at 5, folds
-    CHECK(g_launches.back().fold && !g_launches.back().segmented && dl_log_length(h) == 0);
+    CHECK(g_launches.back().L == 3 && !g_launches.back().segmented && dl_log_length(h) == 0);
     CHECK(dl_decode_tokens(h, toks.data(), 4, nullptr) == DL_OK);  // L 0 -> 4
     CHECK(dl_decode_tokens(h, toks.data(), 8, nullptr) == DL_OK);  // L 4 -> passes the end twice -> 2
     CHECK(g_launches.back().segmented && g_launches.back().L == 4 && g_launches.back().K == 8);
     CHECK(dl_log_length(h) == (4 + 8) % C);
+    CHECK(dl_decode_tokens(h, toks.data(), 5, nullptr) == DL_OK);  // L 2 -> passes the end once -> 2
+    CHECK(!g_launches.back().segmented && g_launches.back().L == 2 && g_launches.back().K == 5);
+    CHECK(dl_log_length(h) == (2 + 5) % C);
     const size_t before = g_launches.size();
     CHECK(dl_decode_tokens(h, toks.data(), 1, nullptr) == DL_OK);  // one token: the single-token kernel
     CHECK(g_launches.size() == before + 1 && g_launches.back().kind == dlk::KIND_STEP);
@@ -218,6 +221,11 @@ static void check_slots(int op) {
     CHECK(g_launches.back().kind == dlk::KIND_CHUNK && g_launches.back().segmented && g_launches.back().slots);
     CHECK(g_launches.back().step == (unsigned)steps);
     steps += 7;
+    for (int b = 0; b < B; ++b) CHECK(dl_slot_log_length(h, b) == (steps - origin[b]) % C);
+    CHECK(dl_decode_tokens(h, toks.data(), 3, nullptr) == DL_OK);  // K <= C: at most one fold per slot
+    CHECK(g_launches.back().kind == dlk::KIND_CHUNK && !g_launches.back().segmented && g_launches.back().slots);
+    CHECK(g_launches.back().step == (unsigned)steps);
+    steps += 3;
     for (int b = 0; b < B; ++b) CHECK(dl_slot_log_length(h, b) == (steps - origin[b]) % C);
     // one slot folded early: only its log empties
     int target = -1;

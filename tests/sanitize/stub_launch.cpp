@@ -26,7 +26,7 @@ hipError_t launch_chunk(int, int DV, int cmax, const ChunkParams &p, hipStream_t
     Launch l = {};
     l.kind = KIND_CHUNK;
     l.op = OP, l.dk = DK, l.dv = DV, l.mode = -1, l.cmax = cmax, l.L = p.L, l.C = p.C, l.N = p.N, l.K = p.K;
-    l.fold = p.fold, l.segmented = p.segmented, l.slots = p.slot_base != nullptr, l.step = p.step;
+    l.segmented = p.segmented, l.slots = p.slot_base != nullptr, l.step = p.step;
     g_launches.push_back(l);
     return hipSuccess;
 }

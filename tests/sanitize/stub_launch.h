@@ -12,7 +12,7 @@ enum { KIND_STEP = 0, KIND_CHUNK = 1, KIND_SLOT_SET = 2 };
 struct Launch {
     int kind;
     // KIND_STEP / KIND_CHUNK
-    int op, dk, dv, mode, cmax, L, C, N, K, fold, segmented;
+    int op, dk, dv, mode, cmax, L, C, N, K, segmented;
     bool slots, prep;
     unsigned step;
     // KIND_SLOT_SET

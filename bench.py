@@ -83,11 +83,32 @@ def measured_traffic(workload):
     return float(m_bytes.group(1))
 
 
+# Untimed warm-up before every timed region, in ms of back-to-back launches.
+# Measured on MI355X: the first ~25 ms of load after an idle spell run up to
+# a few percent slower (per-slot multi-token calls up to 18 %), then the
+# times settle.
+WARM_MS = 40
+
+
+def warm_up(run_batch, sync, at_least=3):
+    """Call run_batch() (which launches some work and returns how many units
+    it launched) until at least WARM_MS of it has run and at least at_least
+    units were launched; synchronises after each batch.  Returns the units."""
+    n = 0
+    t0 = time.perf_counter()
+    while n < at_least or (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        n += run_batch()
+        sync()
+    return n
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40, help="timed merge cycles")
-    ap.add_argument("--warmup", type=int, default=3, help="untimed merge cycles")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed merge cycles (default: whole cycles until %d ms of them have run, at "
+                         "least 3; the clocks settle over the first few tens of ms of load)" % WARM_MS)
     ap.add_argument("--workload", default="gdn_b128_h32_d128")
     ap.add_argument("--C", type=int, default=8, help="log capacity = merge interval")
     ap.add_argument("--B", type=int, default=None, help="override the batch (sweep)")
@@ -183,7 +204,17 @@ def main():
     # Every fifth cycle carries events (an event pair costs several
     # microseconds of GPU time here, so instrumenting every cycle would
     # distort the wall-clock value); C = 1 has events around the whole region.
-    tok = run_cycles(args.warmup, 0)
+    if args.warmup is None:
+        box = [0]
+
+        def warm_batch():
+            box[0] = run_cycles(4, box[0])
+            return 4
+        nwarm = warm_up(warm_batch, torch.cuda.synchronize)
+        tok = box[0]
+    else:
+        nwarm = args.warmup
+        tok = run_cycles(nwarm, 0)
     assert st.log_length == 0
     K = args.steps
     torch.cuda.synchronize()
@@ -242,7 +273,7 @@ def main():
         "unit": "us/token",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": nwarm,
         "ms_per_step": round(ms_per_cycle, 4),
         "higher_is_better": False,
         "scaling": "weak",
@@ -308,7 +339,7 @@ def main():
         efn = lib.dl_eager_step
         cref = ctypes.byref(cfg)
         sp = state.data_ptr()
-        for t in range(args.warmup * C):
+        for t in range(nwarm * C):
             efn(cref, sp, eargs[t % T], sptr)
         ne = K * C
         e0 = torch.cuda.Event(enable_timing=True)
@@ -400,25 +431,25 @@ def multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, K, ntok)
     fn = dl.load_library().dl_decode_tokens
     sptr = stream.cuda_stream
     # every call's argument array is built before the timed region
-    nwarm = -(-3 * C // ntok)
     ntimed = -(-K * C // ntok)
     schedule, tok = [], 0
-    for _ in range(nwarm + ntimed):
+    for _ in range(ntimed):
         schedule.append((dl.StepArgs * ntok)(*[one[(tok + i) % T] for i in range(ntok)]))
         tok += ntok
-    L0 = (nwarm * ntok) % C  # the log length when the timed calls start
 
-    def run(lo, hi):
-        for arr in schedule[lo:hi]:
+    def run(arrs):
+        for arr in arrs:
             assert fn(st.handle, arr, ntok, sptr) == 0
+        return len(arrs)
 
-    run(0, nwarm)
+    warm_up(lambda: run(schedule[:8]), torch.cuda.synchronize, at_least=-(-3 * C // ntok))
+    L0 = st.log_length  # the log length when the timed calls start
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    run(nwarm, len(schedule))
+    run(schedule)
     e1.record(stream)
     torch.cuda.synchronize()
     ntokens = ntimed * ntok
@@ -550,27 +581,31 @@ def staggered_multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs
         assert lib.dl_decode_step(st.handle, ctypes.byref(one[tok % T]), sptr) == 0
         tok += 1
     ncalls = max(1, (K * C) // ntok)
-    warm = 3
+    warm_arrs = [(dl.StepArgs * ntok)(*[one[(i * ntok + j) % T] for j in range(ntok)]) for i in range(8)]
+
+    def warm_batch():
+        for arr in warm_arrs:
+            assert lib.dl_decode_tokens(st.handle, arr, ntok, sptr) == 0
+        return len(warm_arrs)
+    tok += ntok * warm_up(warm_batch, torch.cuda.synchronize)
     calls = []
-    for _ in range(warm + ncalls):
+    for _ in range(ncalls):
         calls.append((tok, (dl.StepArgs * ntok)(*[one[(tok + i) % T] for i in range(ntok)])))
         tok += ntok
-    # modelled bytes of the timed calls: one segmented launch per call, each
-    # slot from its own log length
+    # modelled bytes of the timed calls: one launch per call, each slot from
+    # its own log length
     sh1 = traffic.Shape(sh.op, 1, sh.H, sh.d, sh.in_bytes)
     nbytes = 0
-    for t0, _ in calls[warm:]:
+    for t0, _ in calls:
         for b in range(Bsz):
             nbytes += traffic.call_bytes(sh1, (t0 - start[b]) % C, ntok, C) - sh1.shared()
         nbytes += sh.shared()
-    for _, arr in calls[:warm]:
-        assert lib.dl_decode_tokens(st.handle, arr, ntok, sptr) == 0
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for _, arr in calls[warm:]:
+    for _, arr in calls:
         assert lib.dl_decode_tokens(st.handle, arr, ntok, sptr) == 0
     e1.record(stream)
     torch.cuda.synchronize()

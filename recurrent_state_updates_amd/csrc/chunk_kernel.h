@@ -152,9 +152,11 @@ void chunk_kernel(const ChunkParams p) {
     __shared__ __attribute__((aligned(16))) float s_scale[DK];     // fold: 2^{g_f} per row
     __shared__ __attribute__((aligned(16))) float s_kt[CMAX * DK]; // fold: decayed keys [entry][row], entries < C
     // value factors [entry][col] for the fold (entries < C).  In the
-    // matrix-core form rows L .. L+K-1 first hold the chunk's values (phase D
-    // reads v_t there and writes u_t in its place, or sends it to the new log
-    // past the fold), and row CP takes the writes of token slots past the chunk.
+    // matrix-core form row vrow(t) first holds token t's value: L + t up to
+    // the fold (phase D reads v_t there and writes u_t in its place), rows
+    // from CMAX on for the tokens past it (whose u_t goes to the new log), and
+    // row CP for token slots past the chunk; rows C .. CMAX-1 stay free for
+    // the fold's zero padding.
     __shared__ __attribute__((aligned(16))) float s_x[(MM ? CP + 1 : CMAX) * TV];
     __shared__ float s_coef[NS][KM][CP];  // per side (keys, queries), token and entry
     __shared__ float s_dot[KM];   // <k_t, q_t> or sum r u k
@@ -269,11 +271,12 @@ void chunk_kernel(const ChunkParams p) {
     // matrix-core form: the values go to LDS here so that they hold no registers
     // through phases B and C (every wave writes the same values; no branch, so
     // that no load is sunk past the tile)
+    auto vrow = [&](int t) { return t > tf ? CMAX + t - tf - 1 : L + t; };
     auto stage_tokens = [&]() {
         if (DELTA) s_beta[(c4 == 0 && ke < K) ? ke : KM] = beta_t;
         if constexpr (MM) {
 #pragma unroll
-            for (int t = 0; t < KM; ++t) s_x[(t < K ? L + t : CP) * TV + tid % TV] = to_f32(vraw[t]);
+            for (int t = 0; t < KM; ++t) s_x[(t < K ? vrow(t) : CP) * TV + tid % TV] = to_f32(vraw[t]);
         }
     };
     stage_tokens();
@@ -456,9 +459,7 @@ void chunk_kernel(const ChunkParams p) {
         }
         if (fold) {
             // old value factors of the tile for the fold; zero the fold's entry
-            // slots from C up to a multiple of four (without SEG the
-            // matrix-core form keeps token values in those rows of s_x and
-            // masks them in the fold)
+            // slots from C up to a multiple of four
 #pragma unroll
             for (int j = 0; j < XR; ++j) {
                 const int i = ebase + ESTEP * j;
@@ -470,7 +471,7 @@ void chunk_kernel(const ChunkParams p) {
                 const int i = C + idx / W;
                 const int c = idx % W;
                 if (c < DK) s_kt[i * DK + c] = 0.f;
-                if ((SEG || !MM) && c < TV) s_x[i * TV + c] = 0.f;
+                if (c < TV) s_x[i * TV + c] = 0.f;
             }
         }
         __syncthreads();
@@ -587,7 +588,7 @@ void chunk_kernel(const ChunkParams p) {
                     if (DELTA) yj += s_coef[0][t][L + m] * xs[m];
                     zj += s_coef[ZS][t][L + m] * xs[m];
                 }
-                const float vj = MM ? s_x[(L + t) * TV + jt] : to_f32(vraw[t]);
+                const float vj = MM ? s_x[vrow(t) * TV + jt] : to_f32(vraw[t]);
                 float xnew, o;
                 if (DELTA) {
                     xnew = s_beta[t] * (vj - yj);
@@ -625,9 +626,7 @@ void chunk_kernel(const ChunkParams p) {
                 // = the update of its own s[4 g + q][c].  Each group's rows are stored
                 // as soon as they are done, so that one group's products are live at
                 // a time.
-                // The key slots from C up to a multiple of four are zero; without
-                // SEG the value rows there may hold later tokens' values and are
-                // masked.
+                // The entry slots from C up to a multiple of four are zero.
                 typedef float m4 __attribute__((ext_vector_type(4)));
                 const int m = lane & 15, kr = lane >> 4;
 #pragma unroll
@@ -638,8 +637,7 @@ void chunk_kernel(const ChunkParams p) {
                     for (int c = 0; c < 4; ++c) pc[c] = m4{0.f, 0.f, 0.f, 0.f};
                     for (int e = 0; e < C; e += 4) {
                         const float av = s_kt[(e + kr) * DK + arow];
-                        const f4 bv = SEG || e + kr < C ? *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + cq])
-                                                        : f4{0.f, 0.f, 0.f, 0.f};
+                        const f4 bv = *reinterpret_cast<const f4 *>(&s_x[(e + kr) * TV + cq]);
 #pragma unroll
                         for (int c = 0; c < 4; ++c) pc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[c], pc[c], 0, 0, 0);
                     }

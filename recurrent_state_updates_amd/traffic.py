@@ -96,9 +96,9 @@ def chunk_bytes(sh: Shape, L: int, K: int, fold: bool) -> int:
 
 def call_bytes(sh: Shape, L: int, K: int, C: int) -> int:
     """K tokens in one launch from log length L, folding whenever the log
-    fills and going on from the base in registers: one read of the base, one
-    write per fold, every token in and out, the L old entries replayed, and
-    the entries of the last segment written unless it folds."""
+    fills: one read of the base, one write per fold, every token in and out,
+    the L old entries replayed, and the entries that remain in the log after
+    the call (the tokens past its last fold) written."""
     per = sh.base()
     left, l = K, L
     while left > 0:

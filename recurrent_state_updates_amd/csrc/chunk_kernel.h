@@ -81,10 +81,11 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
 }
 
 // MM selects the matrix-core form of the token products (phase C) and of the
-// fold, at DK = DV = 128.  A workgroup holds a whole head: waves 2h and 2h + 1
-// hold column half h, rows 0-63 and 64-127, 16 lanes per (row, half), so that
-// each 16x16x4 k-step is four rows of one half and two waves' products add up
-// per column.  The vector form (every other shape) holds whole heads as row
+// fold, at DK = DV = 128 or 64.  A workgroup holds a whole head: waves 2h and
+// 2h + 1 hold the 64 columns of column half h (one half at DV = 64), rows
+// 0 .. DK/2 - 1 and DK/2 .. DK - 1, 16 lanes per (row, half), so that each
+// 16x16x4 k-step is four rows of one half and two waves' products add up per
+// column.  The vector form (every other shape) holds whole heads as row
 // passes.
 // Without SEG the call folds at most once (K <= C), at each workgroup's own
 // token on a per-slot handle.  SEG runs calls of more tokens than C (C < 8)
@@ -93,7 +94,7 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
 // form asks for three waves per SIMD, which the compiler meets without
 // spilling (left alone, KDA settles one register above that, at two waves).
 template <int OP, typename TIn, int DK, int DV, int TV, int NT, int CMAX, bool MM, bool SEG>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SEG && MM && CMAX == 8 ? 3 : 1)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SEG && MM && DK == 128 && CMAX == 8 ? 3 : 1)))
 void chunk_kernel(const ChunkParams p) {
     using G = Geom<DK, DV, TV, NT>;
     constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
@@ -106,8 +107,8 @@ void chunk_kernel(const ChunkParams p) {
     constexpr int CP = SEG ? CMAX : CMAX + KM;
     constexpr int KPASS_OLD = (CMAX + EPP - 1) / EPP;  // key-side passes over the old entries (L < C)
     constexpr int KPASS = (CP + EPP - 1) / EPP;         // ... over every entry slot
-    static_assert(!MM || (DK == 128 && DV == 128 && TV == DV && NT == 256 && 2 * KM == 16),
-                  "matrix-core form: whole 128 x 128 heads, 256 threads, 16 product vectors");
+    static_assert(!MM || (DK == DV && (DK == 64 || DK == 128) && TV == DV && NT == 2 * DK && 2 * KM == 16),
+                  "matrix-core form: whole square heads of 64 or 128, 2 DK threads, 16 product vectors");
     // s[i] holds tile row rbase + RSTEP * i; xrow[j] holds log entry ebase + ESTEP * j
     constexpr int RSTEP = MM ? 4 : RPP;
     constexpr int ESTEP = MM ? 8 : RPP;
@@ -187,7 +188,7 @@ void chunk_kernel(const ChunkParams p) {
     const int last = L > 0 ? L - 1 : 0;
     // the thread's rows of the tile, its four columns (from cq, within the
     // tile) and its rows of the old log's value factors
-    const int rbase = MM ? 64 * (wave & 1) + (lane >> 4) : tid / LPR;
+    const int rbase = MM ? (DK / 2) * (wave & 1) + (lane >> 4) : tid / LPR;
     const int cq = MM ? 64 * (wave >> 1) + 4 * (lane & 15) : 4 * (tid % LPR);
     const int ebase = MM ? 4 * (wave & 1) + (lane >> 4) : tid / LPR;
     const int rblk = MM ? (wave & 1) : wave;
@@ -695,32 +696,48 @@ void chunk_kernel(const ChunkParams p) {
     }
 }
 
-// Tile shape of the chunk kernel: one workgroup per head.  At 128 x 128 the
-// matrix-core form: 64 KB over 256 threads of sixteen float4.  Elsewhere the
-// vector form, eight float4 per thread where the head allows it (four at 32
-// x 32, 64 x 32 and 128 x 32), with at least one key-side group of lanes per
-// token (2 DK threads) and one thread per value column: 16 KB over 128
-// threads at 64 x 64, 4 KB over 64 at 32 x 32.
+// Tile shape of the chunk kernel: one workgroup per head.  The matrix-core
+// form holds a square head of 128 or 64 over 2 DK threads (sixteen float4
+// each at 128 x 128, eight at 64 x 64).  The vector form holds eight float4
+// per thread where the head allows it (four at 32 x 32, 64 x 32 and
+// 128 x 32), with at least one key-side group of lanes per token (2 DK
+// threads) and one thread per value column: 16 KB over 128 threads at
+// 64 x 64, 4 KB over 64 at 32 x 32.
 template <int DK, int DV>
 struct ChunkShape {
-    static constexpr bool MM = DK == 128 && DV == 128;
+    static constexpr bool CAN_MM = DK == DV && (DK == 128 || DK == 64);
     static constexpr int TV = DV;
     static constexpr int A = 2 * DK > DV ? 2 * DK : DV;
     static constexpr int B = DK * DV / 32 > 64 ? DK * DV / 32 : 64;
-    static constexpr int NT = MM ? 256 : (A > B ? A : B);
+    static constexpr int NT_VEC = A > B ? A : B;
+    static constexpr int NT_MM = 2 * DK;
+    // The fewest tokens per call that take the matrix-core form, which forms
+    // all 16 product vectors whatever the call's K while the vector form's
+    // work grows with K.  Measured on MI355X (RWKV6 B=128 H=32 d=64, C=8,
+    // us/token, vector -> matrix cores): K=2 10.0 -> 11.1, K=3 7.8 -> 8.2,
+    // K=4 6.3 -> 6.4, K=5 6.13 -> 6.05, K=6 5.5 -> 5.3, K=8 4.6 -> 4.1.  At
+    // 128 x 128 the matrix cores win from two tokens on (a single token goes
+    // to the single-token kernel), so the vector form is not built there.
+    static constexpr int MM_FROM = DK == 128 ? 1 : 5;
 };
 
-// The matrix cores form the token products at 128 x 128 (measured: whole
-// heads there run faster on them than on the vector ALUs from two tokens on;
-// the library sends a single token to the single-token kernel).  The smaller
-// heads stay on the vector ALUs.
 template <int OP, typename TIn, int DK, int DV, int CMAX, bool SEG>
 hipError_t launch_chunk_form(const ChunkParams &p, hipStream_t s) {
     using S = ChunkShape<DK, DV>;
     const unsigned blocks = (unsigned)p.N;
-    hipLaunchKernelGGL((chunk_kernel<OP, TIn, DK, DV, S::TV, S::NT, CMAX, S::MM, SEG>), dim3(blocks), dim3(S::NT),
-                       0, s, p);
-    return hipGetLastError();
+    if constexpr (S::CAN_MM) {
+        if (p.K >= S::MM_FROM) {
+            hipLaunchKernelGGL((chunk_kernel<OP, TIn, DK, DV, S::TV, S::NT_MM, CMAX, true, SEG>), dim3(blocks),
+                               dim3(S::NT_MM), 0, s, p);
+            return hipGetLastError();
+        }
+    }
+    if constexpr (S::MM_FROM > 1 || !S::CAN_MM) {
+        hipLaunchKernelGGL((chunk_kernel<OP, TIn, DK, DV, S::TV, S::NT_VEC, CMAX, false, SEG>), dim3(blocks),
+                           dim3(S::NT_VEC), 0, s, p);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int OP, typename TIn, int DK, int DV, int CMAX>

@@ -48,9 +48,12 @@ def run_chunks(dev, op, dtype, C, sizes, state_steps=()):
     return outs, states, st
 
 
+# d=64 heads take the matrix-core form from five tokens per call and the vector
+# form below: (64, 8, (5, 7, 8)) and (64, 13, (6, 8)) run the former across
+# folds inside calls, (64, 4, (4, 1, 2)) the latter.
 CASES = [(op, dt, d, C, sizes) for op in ("gdn", "kda", "rwkv6") for dt in ("f32", "bf16")
          for d, C, sizes in ((32, 8, (3,)), (64, 4, (4, 1, 2)), (128, 8, (8,)), (128, 13, (5, 7, 1)),
-                             (64, 1, (3,)), (128, 32, (8, 6)))]
+                             (64, 1, (3,)), (128, 32, (8, 6)), (64, 8, (5, 7, 8)), (64, 13, (6, 8)))]
 
 
 @pytest.mark.parametrize("op,dtype,d,C,sizes", CASES)

@@ -622,7 +622,7 @@ def stream_ceilings(dl, S0, Bsz, H, dk, dv, stream, flush, K):
     """The read and the in-place copy of every head at the decode kernels'
     access pattern (dl_probe_stream), on a copy of the state: back to back
     (mean over 4 K launches between two events, as the timed region runs the
-    kernels) and cold, in sequence and isolated (ColdTimer, medians of 12)."""
+    kernels) and cold, in sequence and isolated (ColdTimer, medians of 24)."""
     import numpy as np
     import torch
     state = S0.clone()
@@ -646,8 +646,8 @@ def stream_ceilings(dl, S0, Bsz, H, dk, dv, stream, flush, K):
         e1.record(stream)
         torch.cuda.synchronize()
         warm = e0.elapsed_time(e1) * 1e3 / n
-        iso = float(np.median([timer.isolated(launch) for _ in range(12)]))
-        raw = float(np.median([timer.paired(launch) for _ in range(12)]))
+        iso = float(np.median([timer.isolated(launch) for _ in range(24)]))
+        raw = float(np.median([timer.paired(launch) for _ in range(24)]))
         cold = raw - timer.refill_cost()
         res[name] = {"bytes": moved, "warm_us": round(warm, 2), "warm_GBps": round(moved / (warm * 1e-6) / 1e9, 1),
                      "cold_us": round(cold, 2), "cold_GBps": round(moved / (cold * 1e-6) / 1e9, 1),
@@ -666,7 +666,7 @@ def stream_ceilings(dl, S0, Bsz, H, dk, dv, stream, flush, K):
     e1.record(stream)
     torch.cuda.synchronize()
     res["one_head_launch_us"] = {"back_to_back": round(e0.elapsed_time(e1) * 1e3 / 50, 2),
-                                 "isolated_cold": round(float(np.median([timer.isolated(one) for _ in range(12)])), 2)}
+                                 "isolated_cold": round(float(np.median([timer.isolated(one) for _ in range(24)])), 2)}
     del state
     return res
 
@@ -779,7 +779,7 @@ def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, ntok=0, f
     timer = ColdTimer(torch, stream, flush)
     base = d["S0"].clone()
     st = dl.DeltaLogState(w.op, w.in_dtype, base, C)
-    ncyc = 6
+    ncyc = 20  # a 14 us launch after a 150 us refill: enough cycles that the median settles
     iso = np.zeros((ncyc, C))
     raw = np.zeros((ncyc, C))
     tok = 0

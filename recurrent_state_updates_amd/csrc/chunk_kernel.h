@@ -85,14 +85,15 @@ __device__ __forceinline__ global_ptr<E> group_pick(const T (&arr)[KMAX_TOKENS],
 // 2h + 1 hold the 64 columns of column half h (one half at DV = 64), rows
 // 0 .. DK/2 - 1 and DK/2 .. DK - 1, 16 lanes per (row, half), so that each
 // 16x16x4 k-step is four rows of one half and two waves' products add up per
-// column.  The vector form (every other shape) holds whole heads as row
-// passes.
+// column.  The vector form (the other shapes, and calls of fewer than five
+// tokens at 64 x 64; see ChunkShape) holds whole heads as row passes.
 // Without SEG the call folds at most once (K <= C), at each workgroup's own
 // token on a per-slot handle.  SEG runs calls of more tokens than C (C < 8)
 // as segments in one workgroup: each fold updates the register tile in place
-// and the next tokens start an empty log from it.  The segmented matrix-core
-// form asks for three waves per SIMD, which the compiler meets without
-// spilling (left alone, KDA settles one register above that, at two waves).
+// and the next tokens start an empty log from it.  The segmented 128 x 128
+// matrix-core form asks for three waves per SIMD, which the compiler meets
+// without spilling (left alone, KDA settles one register above that, at two
+// waves).
 template <int OP, typename TIn, int DK, int DV, int TV, int NT, int CMAX, bool MM, bool SEG>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(SEG && MM && DK == 128 && CMAX == 8 ? 3 : 1)))
 void chunk_kernel(const ChunkParams p) {

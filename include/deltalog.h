@@ -162,8 +162,9 @@ dl_status dl_decode_step(dl_state *h, const dl_step_args *args, void *stream);
  * args[0..K-1] are the tokens in order, each as for dl_decode_step, and
  * args[t].out receives o_t.  The tokens share one read of the base in one
  * launch: the log grows by the call's tokens, and when it fills (at any
- * token of the call) the kernel folds it into the base and goes on from the
- * folded base with an empty log.  K == 1 is one dl_decode_step.  The result
+ * token of the call) the kernel folds it into the base and the call's later
+ * tokens start the new log (as many folds as the call fills the log, more
+ * than one only when K > C).  K == 1 is one dl_decode_step.  The result
  * equals K calls of dl_decode_step up to rounding.  The RWKV6 bonus is a
  * per-head parameter, so every token must carry the same bonus pointer
  * (DL_ERR_ARG otherwise).  On a per-slot handle each slot folds at its own

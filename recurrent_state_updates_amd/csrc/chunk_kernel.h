@@ -234,9 +234,13 @@ void chunk_kernel(const ChunkParams p) {
     if (!DELTA) bon4 = *reinterpret_cast<const f4 *>(p.bonus + (size_t)(n % p.H) * DK + c4);
     float glast_s = 0.f;
     f4 glast4 = {0.f, 0.f, 0.f, 0.f};
-    Raw klog[KPASS];
-    float glog_s[KPASS];
-    f4 glog4[KPASS];
+    // the old entries' key side (KPASS_OLD passes) and value rows (XR row
+    // passes); a pass past the L old entries (uniform) is not loaded, so the
+    // bounds above 8 entries cost nothing at short logs.  Pass 0 always
+    // loads (a clamped, valid entry when L = 0).
+    Raw klog[KPASS_OLD];
+    float glog_s[KPASS_OLD];
+    f4 glog4[KPASS_OLD];
     RawX xrow[XR];
     {
         const size_t el = (size_t)n * C + last;
@@ -245,7 +249,8 @@ void chunk_kernel(const ChunkParams p) {
         else
             glast4 = *reinterpret_cast<const f4 *>(p.logG + el * DK + c4);
 #pragma unroll
-        for (int ps = 0; ps < KPASS; ++ps) {
+        for (int ps = 0; ps < KPASS_OLD; ++ps) {
+            if (ps > 0 && ps * EPP >= L) continue;
             const size_t e = (size_t)n * C + min(ps * EPP + ke, last);
             klog[ps] = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.logK) + e * DK + c4);
             if (GDN)
@@ -256,7 +261,7 @@ void chunk_kernel(const ChunkParams p) {
         const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * DV + col0 + cq;
 #pragma unroll
         for (int j = 0; j < XR; ++j)
-            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(ebase + ESTEP * j, last) * DV);
+            if (j == 0 || ESTEP * j < L) xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(ebase + ESTEP * j, last) * DV);
     }
     // the small loads above all go out before the tile's (loads complete in
     // issue order, so one placed after the tile could only be used once the
@@ -516,6 +521,7 @@ void chunk_kernel(const ChunkParams p) {
             }
 #pragma unroll
             for (int j = 0; j < XR; ++j) {
+                if (j > 0 && ESTEP * j >= L) continue;  // a row pass with no old entry (not loaded)
                 // entries at or past L were loaded from a clamped index and may be
                 // anything (an unused slot holds whatever the workspace held): zero
                 // both operands, since 0 * NaN would poison the sum

@@ -343,6 +343,12 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     //     rs + RPP*j), the tile's value side as float4 rows.
     float glast_s = 0.f;
     f4 glast4 = {0.f, 0.f, 0.f, 0.f};
+    // A bound above 8 entries (CMAX 16, 32) spreads the key side over KPASS
+    // passes and the value side over XR row passes; a pass that holds no
+    // logged entry (uniform: it depends only on L) is neither loaded nor
+    // computed.  Pass 0 always runs, so the 8-entry kernels are unchanged.
+    auto pass_used = [&](int ps) { return ps == 0 || ps * EPP < L; };
+    auto row_pass_used = [&](int j) { return j == 0 || RPP * j < L; };
     Raw klog[KPASS];
     float glog_s[KPASS];
     f4 glog4[KPASS];
@@ -355,6 +361,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
             glast4 = *reinterpret_cast<const f4 *>(p.logG + el * DK + c4);
 #pragma unroll
         for (int ps = 0; ps < KPASS; ++ps) {
+            if (!pass_used(ps)) continue;
             const size_t e = (size_t)n * C + min(ps * EPP + ke, last);
             klog[ps] = *reinterpret_cast<const Raw *>(static_cast<const TIn *>(p.logK) + e * DK + c4);
             if (GDN)
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         const TX *xin = static_cast<const TX *>(p.logX) + (size_t)n * C * DV + col0 + 4 * cg;
 #pragma unroll
         for (int j = 0; j < XR; ++j)
-            xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * DV);
+            if (row_pass_used(j)) xrow[j] = *reinterpret_cast<const RawX *>(xin + (size_t)min(rs + RPP * j, last) * DV);
     }
     // A2'. Split replay: this head's prep record (thread t takes floats t,
     //      t + NT, ... of the scaled key | scaled query, and one coefficient).
@@ -460,6 +467,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         float pk[KPASS], pq[KPASS];
 #pragma unroll
         for (int ps = 0; ps < KPASS; ++ps) {
+            if (!pass_used(ps)) continue;
             const int i = ps * EPP + ke;
             const bool valid = i < L;
             const f4 kv = In4<TIn>::unpack(klog[ps]);
@@ -476,6 +484,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         if (TOKEN) {
 #pragma unroll
             for (int ps = 0; ps < KPASS; ++ps) {
+                if (!pass_used(ps)) continue;
                 pk[ps] = group_sum_valu<KL>(pk[ps]);
                 pq[ps] = group_sum_valu<KL>(pq[ps]);
             }
@@ -483,7 +492,7 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
 #pragma unroll
                 for (int ps = 0; ps < KPASS; ++ps) {
                     const int i = ps * EPP + ke;
-                    if (i < L) {
+                    if (pass_used(ps) && i < L) {
                         s_coef[0][i] = pk[ps];
                         s_coef[1][i] = pq[ps];
                     }

@@ -335,6 +335,22 @@ double dl_predict_token_us(const dl_config *cfg, double read_gbps, double copy_g
  * invalid cfg or max_c. */
 int dl_choose_capacity(const dl_config *cfg, int max_c, double read_gbps, double copy_gbps);
 
+/* The same model with a rate per kernel family.  A capacity runs the
+ * kernels built for a log of 8 (C <= 8), 16 (C <= 16) or 32 entries; the
+ * larger bounds hold more key-side registers per lane, which costs some
+ * shapes (the 64 x 64 heads) more than the bytes show.  read_gbps[f] and
+ * copy_gbps[f] are the rates the family f = 0, 1, 2 (8, 16, 32 entries)
+ * reaches for its appends and its fold -- for instance the stream ceilings
+ * scaled by the measured over modelled time of one capacity of that family
+ * (bench.py --capacity-study).  A rate <= 0 selects the default ceiling as
+ * above.  Both arrays hold three values and must not be NULL
+ * (dl_predict_token_us_bounds returns a negative value,
+ * dl_choose_capacity_bounds DL_ERR_ARG).  dl_predict_token_us and
+ * dl_choose_capacity are these with one rate for all three families.
+ * Host-only. */
+double dl_predict_token_us_bounds(const dl_config *cfg, const double read_gbps[3], const double copy_gbps[3]);
+int dl_choose_capacity_bounds(const dl_config *cfg, int max_c, const double read_gbps[3], const double copy_gbps[3]);
+
 /* Release a handle (NULL is allowed).  Device buffers are not touched. */
 void dl_state_destroy(dl_state *h);
 

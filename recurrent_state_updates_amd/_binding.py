@@ -85,6 +85,9 @@ def load_library():
         "dl_slot_merge": (i, [vp, i, vp]),
         "dl_predict_token_us": (ctypes.c_double, [cp, ctypes.c_double, ctypes.c_double]),
         "dl_choose_capacity": (i, [cp, i, ctypes.c_double, ctypes.c_double]),
+        "dl_predict_token_us_bounds": (ctypes.c_double, [cp, ctypes.POINTER(ctypes.c_double),
+                                                         ctypes.POINTER(ctypes.c_double)]),
+        "dl_choose_capacity_bounds": (i, [cp, i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]),
         "dl_prep_bytes": (sz, [cp]),
         "dl_set_split_replay": (i, [vp, vp, sz]),
         "dl_graph_capture_cycle": (i, [ctypes.POINTER(vp), vp, ap]),
@@ -216,6 +219,28 @@ def dl_predict_token_us(cfg, read_gbps=0.0, copy_gbps=0.0):
 
 def dl_choose_capacity(cfg, max_c=DL_MAX_CAPACITY, read_gbps=0.0, copy_gbps=0.0):
     c = int(load_library().dl_choose_capacity(ctypes.byref(cfg), max_c, read_gbps, copy_gbps))
+    if c < 0:
+        _check(c)
+    return c
+
+
+def _three(rates):
+    r = [float(x) for x in rates]
+    if len(r) != 3:
+        raise ValueError("three rates are needed: the kernels built for 8, 16 and 32 log entries")
+    return (ctypes.c_double * 3)(*r)
+
+
+def dl_predict_token_us_bounds(cfg, read_gbps, copy_gbps):
+    us = float(load_library().dl_predict_token_us_bounds(ctypes.byref(cfg), _three(read_gbps), _three(copy_gbps)))
+    if us < 0:
+        raise DeltaLogError(DL_ERR_ARG, dl_last_error() or "invalid config")
+    return us
+
+
+def dl_choose_capacity_bounds(cfg, read_gbps, copy_gbps, max_c=DL_MAX_CAPACITY):
+    c = int(load_library().dl_choose_capacity_bounds(ctypes.byref(cfg), max_c, _three(read_gbps),
+                                                     _three(copy_gbps)))
     if c < 0:
         _check(c)
     return c

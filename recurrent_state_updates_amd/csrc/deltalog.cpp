@@ -774,34 +774,51 @@ dl_status dl_eager_step(const dl_config *cfg, float *state, const dl_step_args *
 }
 
 double dl_predict_token_us(const dl_config *cfg, double read_gbps, double copy_gbps) {
+    const double read[3] = {read_gbps, read_gbps, read_gbps};
+    const double copy[3] = {copy_gbps, copy_gbps, copy_gbps};
+    return dl_predict_token_us_bounds(cfg, read, copy);
+}
+
+double dl_predict_token_us_bounds(const dl_config *cfg, const double read_gbps[3], const double copy_gbps[3]) {
     size_t heads = 0;
+    if (!read_gbps || !copy_gbps) return -1.0;
     if (check_config(cfg, &heads) != DL_OK) return -1.0;
+    // the rates of the kernels this capacity runs (built for 8, 16 or 32 entries)
+    const int fam = cfg->C <= 8 ? 0 : (cfg->C <= 16 ? 1 : 2);
+    double read = read_gbps[fam], copy = copy_gbps[fam];
     // defaults: the stream ceilings of the kernels' own access pattern on
     // MI355X, measured in sequence with a cold Infinity Cache (bench.py's
     // `ceilings`, GDN B=128 H=32 d=128): a read of every head, an in-place copy
-    if (read_gbps <= 0) read_gbps = 6760.0;
-    if (copy_gbps <= 0) copy_gbps = 5580.0;
+    if (read <= 0) read = 6760.0;
+    if (copy <= 0) copy = 5580.0;
     const HeadBytes b = head_bytes(cfg);
     const double n = (double)heads;
     const int C = cfg->C;
     double us = 0.0;
     for (int L = 0; L + 1 < C; ++L)  // appends
-        us += (n * (b.base + b.token + b.out + (L + 1) * b.entry) + b.shared) / (read_gbps * 1e3);
-    us += (n * (2.0 * b.base + b.token + b.out + (C - 1) * b.entry) + b.shared) / (copy_gbps * 1e3);
+        us += (n * (b.base + b.token + b.out + (L + 1) * b.entry) + b.shared) / (read * 1e3);
+    us += (n * (2.0 * b.base + b.token + b.out + (C - 1) * b.entry) + b.shared) / (copy * 1e3);
     return us / C;
 }
 
 int dl_choose_capacity(const dl_config *cfg, int max_c, double read_gbps, double copy_gbps) {
+    const double read[3] = {read_gbps, read_gbps, read_gbps};
+    const double copy[3] = {copy_gbps, copy_gbps, copy_gbps};
+    return dl_choose_capacity_bounds(cfg, max_c, read, copy);
+}
+
+int dl_choose_capacity_bounds(const dl_config *cfg, int max_c, const double read_gbps[3], const double copy_gbps[3]) {
     size_t heads = 0;
     dl_status st = check_config(cfg, &heads);
     if (st != DL_OK) return st;
     if (max_c < 1 || max_c > DL_MAX_CAPACITY) return fail(DL_ERR_SHAPE, "max_c must lie in [1, 32]");
+    if (!read_gbps || !copy_gbps) return fail(DL_ERR_ARG, "read_gbps and copy_gbps must point to three rates each");
     dl_config c = *cfg;
     int best = 1;
     double best_us = 0.0;
     for (int C = 1; C <= max_c; ++C) {
         c.C = C;
-        const double us = dl_predict_token_us(&c, read_gbps, copy_gbps);
+        const double us = dl_predict_token_us_bounds(&c, read_gbps, copy_gbps);
         if (C == 1 || us < best_us) {
             best = C;
             best_us = us;

@@ -1,4 +1,6 @@
 """The traffic model: byte counts per launch and the capacity chooser (CPU only)."""
+import ctypes
+
 import pytest
 
 import recurrent_state_updates_amd as dl
@@ -83,3 +85,53 @@ def test_call_bytes_of_segmented_launches():
                     assert got == want, (op, C, L, K)
     sh = T.Shape("gdn", 128, 32, 128, 2)
     assert T.multi_token_bytes(sh, 8, 8, 16) == 2 * T.chunk_bytes(sh, 0, 8, True)
+
+
+def _family(C):
+    return 0 if C <= 8 else (1 if C <= 16 else 2)
+
+
+@pytest.mark.parametrize("op,d", [("gdn", 128), ("kda", 128), ("rwkv6", 64)])
+def test_family_rates_price_each_capacity_with_its_own_kernels(op, d):
+    """Each capacity is priced at the rates of the kernels it runs: the ones
+    built for 8, 16 or 32 entries.  With one rate for all three the model is
+    dl_predict_token_us."""
+    read, copy = (6100.0, 5900.0, 5200.0), (5000.0, 4800.0, 4300.0)
+    for C in (1, 7, 8, 9, 13, 16, 17, 32):
+        cfg = dl.make_config(op, "bf16", 64, 32, d, d, C)
+        f = _family(C)
+        assert dl.dl_predict_token_us_bounds(cfg, read, copy) == pytest.approx(
+            _predict_py(op, 64, 32, d, C, read[f], copy[f]), rel=1e-12)
+        assert dl.dl_predict_token_us_bounds(cfg, (6000.0,) * 3, (5000.0,) * 3) == \
+            dl.dl_predict_token_us(cfg, 6000.0, 5000.0)
+
+
+def test_family_rates_move_the_pick_to_the_kernels_that_run_faster():
+    """The 64 x 64 heads at B=128: with one rate for every capacity the byte
+    model picks a capacity of the 16-entry family; with that family 3 % slower
+    (as measured for RWKV6) the pick stays with the 8-entry kernels.  Both
+    picks are the argmin of the Python model priced the same way."""
+    cfg = dl.make_config("rwkv6", "bf16", 128, 32, 64, 64, 8)
+    one = dl.dl_choose_capacity(cfg, dl.DL_MAX_CAPACITY, 8000.0, 6000.0)
+    assert 8 < one <= 16
+    read, copy = (8000.0, 0.97 * 8000.0, 0.97 * 8000.0), (6000.0, 0.97 * 6000.0, 0.97 * 6000.0)
+    got = dl.dl_choose_capacity_bounds(cfg, read, copy)
+    preds = {C: _predict_py("rwkv6", 128, 32, 64, C, read[_family(C)], copy[_family(C)]) for C in range(1, 33)}
+    assert got == min(preds, key=preds.get) == 8
+    assert dl.dl_choose_capacity_bounds(cfg, (8000.0,) * 3, (6000.0,) * 3) == one
+    # max_c caps the search as for the one-rate chooser
+    assert dl.dl_choose_capacity_bounds(cfg, (8000.0,) * 3, (6000.0,) * 3, max_c=4) == \
+        dl.dl_choose_capacity(cfg, 4, 8000.0, 6000.0)
+
+
+def test_family_rates_reject_invalid():
+    cfg = dl.make_config("gdn", "bf16", 1, 1, 128, 128, 8)
+    with pytest.raises(ValueError):
+        dl.dl_choose_capacity_bounds(cfg, (1.0, 2.0), (1.0, 2.0, 3.0))
+    with pytest.raises(dl.DeltaLogError):
+        dl.dl_choose_capacity_bounds(cfg, (1.0,) * 3, (1.0,) * 3, max_c=33)
+    with pytest.raises(dl.DeltaLogError):
+        dl.dl_predict_token_us_bounds(B.Config(0, 1, 0, 32, 128, 128, 8), (1.0,) * 3, (1.0,) * 3)
+    lib = dl.load_library()
+    assert lib.dl_predict_token_us_bounds(ctypes.byref(cfg), None, None) < 0
+    assert lib.dl_choose_capacity_bounds(ctypes.byref(cfg), 8, None, None) == B.DL_ERR_ARG

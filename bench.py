@@ -16,9 +16,10 @@ Printed: ONE JSON line.  Besides the contract fields it carries
                 Infinity Cache was refilled with another buffer (the state of
                 the other layers of a model would pass through it between two
                 launches of one layer)
-  ceilings      what the GPU streams at the kernels' own access pattern: a read
-                and an in-place copy of every head with the decode kernels'
-                workgroup shape, mapping and loads, back to back and cold
+  ceilings      what the GPU streams at the kernels' own access pattern: a read,
+                an in-place copy and a write of every head with the decode
+                kernels' workgroup shape, mapping and loads, back to back and
+                cold
 Usage: python bench.py [--steps K] [--warmup W] [--workload NAME] [--C c]
                        [--no-cold] [--report PATH] [--no-cpu] [--capacity-study]
 """
@@ -621,10 +622,11 @@ def staggered_multi_token_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs
 
 
 def stream_ceilings(dl, S0, Bsz, H, dk, dv, stream, flush, K):
-    """The read and the in-place copy of every head at the decode kernels'
-    access pattern (dl_probe_stream), on a copy of the state: back to back
-    (mean over 4 K launches between two events, as the timed region runs the
-    kernels) and cold, in sequence and isolated (ColdTimer, medians of 24)."""
+    """The read, the in-place copy and the write of every head at the decode
+    kernels' access pattern (dl_probe_stream), on a copy of the state: back
+    to back (mean over 4 K launches between two events, as the timed region
+    runs the kernels) and cold, in sequence and isolated (ColdTimer, medians
+    of 24)."""
     import numpy as np
     import torch
     state = S0.clone()
@@ -633,7 +635,7 @@ def stream_ceilings(dl, S0, Bsz, H, dk, dv, stream, flush, K):
     nbytes = Bsz * H * dk * dv * 4
     timer = ColdTimer(torch, stream, flush)
     res = {"state_bytes": nbytes}
-    for name, mode, moved in (("read", dl.DL_PROBE_READ, nbytes), ("copy", dl.DL_PROBE_COPY, 2 * nbytes)):
+    def measure(name, mode, moved):
         def launch():
             dl.dl_probe_stream(mode, state.data_ptr(), Bsz, H, dk, dv, sink.data_ptr(), sptr)
         for _ in range(3):
@@ -655,7 +657,12 @@ def stream_ceilings(dl, S0, Bsz, H, dk, dv, stream, flush, K):
                      "cold_us": round(cold, 2), "cold_GBps": round(moved / (cold * 1e-6) / 1e9, 1),
                      "isolated_cold_us": round(iso, 2),
                      "isolated_cold_GBps": round(moved / (iso * 1e-6) / 1e9, 1)}
+
+    measure("read", dl.DL_PROBE_READ, nbytes)
+    measure("copy", dl.DL_PROBE_COPY, 2 * nbytes)
     assert torch.equal(state, S0), "the copy probe must leave the state unchanged"
+    # the write side alone (overwrites this copy of the state)
+    measure("write", dl.DL_PROBE_WRITE, nbytes)
     # the fixed cost of a launch: the read probe over one head, back to back and isolated
     def one():
         dl.dl_probe_stream(dl.DL_PROBE_READ, state.data_ptr(), 1, 1, dk, dv, sink.data_ptr(), sptr)

@@ -114,7 +114,7 @@ def _check(status):
         raise DeltaLogError(status, msg)
 
 
-DL_PROBE_READ, DL_PROBE_COPY = 0, 1
+DL_PROBE_READ, DL_PROBE_COPY, DL_PROBE_WRITE = 0, 1, 2
 
 
 def dl_probe_last_error():

@@ -3,7 +3,8 @@
 // 16-byte nontemporal loads (and stores) as the append and the
 // decode-and-fold, with none of their other work.  These bound the path from
 // above: an append cannot beat a read of its heads, a fold cannot beat an
-// in-place copy of them.
+// in-place copy of them.  A write of every head (no read) shows what the
+// write side alone streams, beside the copy that mixes the two.
 #include "../../include/deltalog_probe.h"
 
 #include <hip/hip_runtime.h>
@@ -14,12 +15,13 @@
 
 namespace dlk {
 
-// COPY = false: read every head once and keep one conditional store, which
-// the compiler cannot drop without the sum (a sum of finite state values
-// equal to NaN never happens).  COPY = true: read and write every head back
-// in place, multiplied by `one` (1.0f at run time: the values do not change,
-// but the compiler cannot drop a store it does not know to be redundant).
-template <int DK, int DV, int NT, bool COPY>
+// KIND = DL_PROBE_READ: read every head once and keep one conditional store,
+// which the compiler cannot drop without the sum (a sum of finite state
+// values equal to NaN never happens).  DL_PROBE_COPY: read and write every
+// head back in place, multiplied by `one` (1.0f at run time: the values do
+// not change, but the compiler cannot drop a store it does not know to be
+// redundant).  DL_PROBE_WRITE: write `one` to every element, no read.
+template <int DK, int DV, int NT, int KIND>
 __global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, int N, float one) {
     using G = Geom<DK, DV, DV, NT>;
     int n, tile;
@@ -27,10 +29,16 @@ __global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, in
     const int tid = threadIdx.x;
     const int cg = tid % G::LPR, rs = tid / G::LPR;
     f4 *p4 = reinterpret_cast<f4 *>(state) + (size_t)n * (DK * DV / 4) + (size_t)rs * (DV / 4) + cg;
+    if constexpr (KIND == DL_PROBE_WRITE) {
+        const f4 c = {one, one, one, one};
+#pragma unroll
+        for (int i = 0; i < G::R; ++i) __builtin_nontemporal_store(c, p4 + (size_t)i * G::RPP * (DV / 4));
+        return;
+    }
     f4 s[G::R];
 #pragma unroll
     for (int i = 0; i < G::R; ++i) s[i] = __builtin_nontemporal_load(p4 + (size_t)i * G::RPP * (DV / 4));
-    if constexpr (COPY) {
+    if constexpr (KIND == DL_PROBE_COPY) {
 #pragma unroll
         for (int i = 0; i < G::R; ++i) __builtin_nontemporal_store(s[i] * one, p4 + (size_t)i * G::RPP * (DV / 4));
     } else {
@@ -42,21 +50,23 @@ __global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, in
 }
 
 template <int DK, int DV>
-hipError_t launch_probe(int copy, float *state, float *sink, int N, hipStream_t s) {
+hipError_t launch_probe(int kind, float *state, float *sink, int N, hipStream_t s) {
     constexpr int NT = Shape<DK, DV, MODE_APPEND>::NT;
-    if (copy)
-        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, true>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
+    if (kind == DL_PROBE_COPY)
+        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, DL_PROBE_COPY>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
+    else if (kind == DL_PROBE_WRITE)
+        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, DL_PROBE_WRITE>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
     else
-        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, false>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
+        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, DL_PROBE_READ>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
     return hipGetLastError();
 }
 
 template <int DK>
-hipError_t probe_value_width(int dv, int copy, float *state, float *sink, int N, hipStream_t s) {
+hipError_t probe_value_width(int dv, int kind, float *state, float *sink, int N, hipStream_t s) {
     switch (dv) {
-        case 32: return launch_probe<DK, 32>(copy, state, sink, N, s);
-        case 64: return launch_probe<DK, 64>(copy, state, sink, N, s);
-        case 128: return launch_probe<DK, 128>(copy, state, sink, N, s);
+        case 32: return launch_probe<DK, 32>(kind, state, sink, N, s);
+        case 64: return launch_probe<DK, 64>(kind, state, sink, N, s);
+        case 128: return launch_probe<DK, 128>(kind, state, sink, N, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -71,8 +81,8 @@ extern "C" {
 
 int dl_probe_stream(int mode, float *state, int B, int H, int dk, int dv, float *sink, void *stream) {
     auto built = [](int w) { return w == 32 || w == 64 || w == 128; };
-    if (mode != DL_PROBE_READ && mode != DL_PROBE_COPY) {
-        g_probe_error = "mode must be DL_PROBE_READ or DL_PROBE_COPY";
+    if (mode != DL_PROBE_READ && mode != DL_PROBE_COPY && mode != DL_PROBE_WRITE) {
+        g_probe_error = "mode must be DL_PROBE_READ, DL_PROBE_COPY or DL_PROBE_WRITE";
         return -1;
     }
     if (!state || !sink || (reinterpret_cast<uintptr_t>(state) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 3u)) {
@@ -89,12 +99,11 @@ int dl_probe_stream(int mode, float *state, int B, int H, int dk, int dv, float 
     }
     const int N = B * H;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const int copy = mode == DL_PROBE_COPY;
     hipError_t e;
     switch (dk) {
-        case 32: e = dlk::probe_value_width<32>(dv, copy, state, sink, N, s); break;
-        case 64: e = dlk::probe_value_width<64>(dv, copy, state, sink, N, s); break;
-        default: e = dlk::probe_value_width<128>(dv, copy, state, sink, N, s); break;
+        case 32: e = dlk::probe_value_width<32>(dv, mode, state, sink, N, s); break;
+        case 64: e = dlk::probe_value_width<64>(dv, mode, state, sink, N, s); break;
+        default: e = dlk::probe_value_width<128>(dv, mode, state, sink, N, s); break;
     }
     if (e != hipSuccess) {
         g_probe_error = std::string("kernel launch failed: ") + hipGetErrorString(e);

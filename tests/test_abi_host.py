@@ -360,7 +360,8 @@ def test_largest_head_count_is_accepted():
 def test_probe_validates_on_the_host():
     lib = B.load_library()
     sink = FAKE + 0x50000000
-    assert lib.dl_probe_stream(2, FAKE, 1, 1, 64, 64, sink, None) == -1          # bad mode
+    assert lib.dl_probe_stream(3, FAKE, 1, 1, 64, 64, sink, None) == -1          # bad mode
+    assert lib.dl_probe_stream(-1, FAKE, 1, 1, 64, 64, sink, None) == -1         # bad mode
     assert lib.dl_probe_stream(0, FAKE + 8, 1, 1, 64, 64, sink, None) == -1      # misaligned state
     assert lib.dl_probe_stream(0, FAKE, 1, 1, 64, 64, 0, None) == -1             # no sink
     assert lib.dl_probe_stream(1, FAKE, 0, 1, 64, 64, sink, None) == -2          # empty batch

@@ -49,6 +49,7 @@ def metric_name(op, B, H, dk, dv, C):
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "append_{workload}_c8_traffic.md")
 # the sources each kind of counter summary is tied to
 KERNEL_SOURCES = ["recurrent_state_updates_amd/csrc/step_kernel.h",
+                  "recurrent_state_updates_amd/csrc/step_launch.h",
                   "recurrent_state_updates_amd/csrc/launch.h"]
 CHUNK_SOURCES = KERNEL_SOURCES + ["recurrent_state_updates_amd/csrc/chunk_kernel.h"]
 
@@ -56,7 +57,8 @@ CHUNK_SOURCES = KERNEL_SOURCES + ["recurrent_state_updates_amd/csrc/chunk_kernel
 def kernel_source_hash(sources=None):
     """First 16 hex digits of the SHA-256 of the kernel sources with comments
     and blank space removed: the counters are tied to the code, not to its
-    commentary.  The single-token summaries hash step_kernel.h and launch.h,
+    commentary.  The single-token summaries hash step_kernel.h, step_launch.h
+    (which decides the launch shape) and launch.h,
     the multi-token ones chunk_kernel.h as well (CHUNK_SOURCES)."""
     h = hashlib.sha256()
     for rel in sources or KERNEL_SOURCES:

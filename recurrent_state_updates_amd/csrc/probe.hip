@@ -11,7 +11,7 @@
 
 #include <string>
 
-#include "step_kernel.h"
+#include "step_launch.h"
 
 namespace dlk {
 
@@ -21,14 +21,12 @@ namespace dlk {
 // head back in place, multiplied by `one` (1.0f at run time: the values do
 // not change, but the compiler cannot drop a store it does not know to be
 // redundant).  DL_PROBE_WRITE: write `one` to every element, no read.
-template <int DK, int DV, int NT, int KIND>
-__global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, int N, float one) {
-    using G = Geom<DK, DV, DV, NT>;
-    int n, tile;
-    block_to_tile<StepOrder<DK, DV>::XCD>(blockIdx.x, N, 1, n, tile);
+template <int DK, int DV, int TV, int NT, int KIND>
+__device__ __forceinline__ void probe_body(float *state, float *sink, int n, int tile, float one) {
+    using G = Geom<DK, DV, TV, NT>;
     const int tid = threadIdx.x;
     const int cg = tid % G::LPR, rs = tid / G::LPR;
-    f4 *p4 = reinterpret_cast<f4 *>(state) + (size_t)n * (DK * DV / 4) + (size_t)rs * (DV / 4) + cg;
+    f4 *p4 = reinterpret_cast<f4 *>(state) + (size_t)n * (DK * DV / 4) + tile * (TV / 4) + (size_t)rs * (DV / 4) + cg;
     if constexpr (KIND == DL_PROBE_WRITE) {
         const f4 c = {one, one, one, one};
 #pragma unroll
@@ -49,15 +47,38 @@ __global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, in
     }
 }
 
+// One workgroup per head in the decode kernels' block order; at 128 x 128,
+// when the decode kernels split the launch's last heads into half-width
+// tiles (TAIL_HEADS_128, step_launch.h), the probe does the same.
+template <int DK, int DV, int NT, int KIND>
+__global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, int N, int tail, float one) {
+    const int nf = N - tail;
+    const int b = blockIdx.x;
+    int n, tile;
+    if (b < nf) {
+        block_to_tile<StepOrder<DK, DV>::XCD>(b, nf, 1, n, tile);
+        probe_body<DK, DV, DV, NT, KIND>(state, sink, n, 0, one);
+    } else if constexpr (DV % 8 == 0) {
+        block_to_tile<true>(b - nf, tail, 2, n, tile);
+        probe_body<DK, DV, DV / 2, NT, KIND>(state, sink, nf + n, tile, one);
+    }
+}
+
+template <int DK, int DV, int KIND>
+void launch_probe_kind(float *state, float *sink, int N, hipStream_t s) {
+    constexpr int NT = Shape<DK, DV, MODE_APPEND>::NT;
+    const int tail = (DK == 128 && DV == 128 && N >= 4 * TAIL_HEADS_128) ? TAIL_HEADS_128 : 0;
+    hipLaunchKernelGGL((probe_kernel<DK, DV, NT, KIND>), dim3(N + tail), dim3(NT), 0, s, state, sink, N, tail, 1.0f);
+}
+
 template <int DK, int DV>
 hipError_t launch_probe(int kind, float *state, float *sink, int N, hipStream_t s) {
-    constexpr int NT = Shape<DK, DV, MODE_APPEND>::NT;
     if (kind == DL_PROBE_COPY)
-        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, DL_PROBE_COPY>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
+        launch_probe_kind<DK, DV, DL_PROBE_COPY>(state, sink, N, s);
     else if (kind == DL_PROBE_WRITE)
-        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, DL_PROBE_WRITE>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
+        launch_probe_kind<DK, DV, DL_PROBE_WRITE>(state, sink, N, s);
     else
-        hipLaunchKernelGGL((probe_kernel<DK, DV, NT, DL_PROBE_READ>), dim3(N), dim3(NT), 0, s, state, sink, N, 1.0f);
+        launch_probe_kind<DK, DV, DL_PROBE_READ>(state, sink, N, s);
     return hipGetLastError();
 }
 

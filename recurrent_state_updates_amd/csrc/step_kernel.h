@@ -249,8 +249,7 @@ __device__ __forceinline__ float column_sum_valu(float x) {
 // with no branch and no dependence between them, so that one memory
 // round-trip covers them all; only then does any arithmetic start.
 template <int OP, typename TIn, int DK, int DV, int TV, int NT, int MODE, int CMAX>
-__global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
-    const StepParams p) {
+__device__ __forceinline__ void step_body(const StepParams &p, const int n, const int tile) {
     using G = Geom<DK, DV, TV, NT>;
     constexpr int NTILE = G::NTILE, LPR = G::LPR, RPP = G::RPP, R = G::R, NW = G::NW;
     constexpr int KL = G::KL, EPP = G::EPP;
@@ -288,8 +287,6 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    int n, tile;
-    block_to_tile<StepOrder<DK, DV>::XCD>(blockIdx.x, p.N, PREP ? 1 : NTILE, n, tile);
     const int C = p.C;
     int L = LOGGED ? p.L : 0;
     if (LOGGED && p.slot_base != nullptr) {
@@ -640,6 +637,32 @@ __global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(
         f4 *dst4 = reinterpret_cast<f4 *>(p.dst) + tile4;
 #pragma unroll
         for (int i = 0; i < R; ++i) __builtin_nontemporal_store(acc[i], dst4 + (size_t)i * RPP * (DV / 4));
+    }
+}
+
+// One workgroup per (head, tile), mapped as block_to_tile says.
+template <int OP, typename TIn, int DK, int DV, int TV, int NT, int MODE, int CMAX>
+__global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel(const StepParams p) {
+    int n, tile;
+    block_to_tile<StepOrder<DK, DV>::XCD>(blockIdx.x, p.N, MODE == MODE_PREP ? 1 : DV / TV, n, tile);
+    step_body<OP, TIn, DK, DV, TV, NT, MODE, CMAX>(p, n, tile);
+}
+
+// Whole heads, except the last `tail` heads of the launch, which run as two
+// half-width tiles each on the same number of threads.  Workgroups start in
+// dispatch order, so the last ones to start set the launch's end; with half
+// a head's bytes each they end about half a workgroup lifetime sooner.
+template <int OP, typename TIn, int DK, int DV, int NT, int MODE, int CMAX>
+__global__ __launch_bounds__(NT) DLK_OCCUPANCY void step_kernel_tail(const StepParams p, const int tail) {
+    const int nf = p.N - tail;
+    const int b = blockIdx.x;
+    int n, tile;
+    if (b < nf) {
+        block_to_tile<true>(b, nf, 1, n, tile);
+        step_body<OP, TIn, DK, DV, DV, NT, MODE, CMAX>(p, n, 0);
+    } else {
+        block_to_tile<true>(b - nf, tail, 2, n, tile);
+        step_body<OP, TIn, DK, DV, DV / 2, NT, MODE, CMAX>(p, nf + n, tile);
     }
 }
 

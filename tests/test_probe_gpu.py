@@ -24,9 +24,11 @@ def gpu():
     yield
 
 
-@pytest.mark.parametrize("dk,dv", [(a, b) for a in (32, 64, 128) for b in (32, 64, 128)])
-def test_probes_touch_exactly_the_state(dk, dv):
-    Bsz, H = 3, 5
+@pytest.mark.parametrize("dk,dv,Bsz,H", [(a, b, 3, 5) for a in (32, 64, 128) for b in (32, 64, 128)]
+                         + [(128, 128, 64, 32)])
+def test_probes_touch_exactly_the_state(dk, dv, Bsz, H):
+    """Small batches, and a batch of 2048 heads of 128 x 128, whose last 512
+    the probes (like the decode kernels) read and write as half-width tiles."""
     n = Bsz * H * dk * dv
     g = torch.Generator(device="cpu").manual_seed(dk * 1000 + dv)
     guard = 4096  # floats before and after the tensor, which no probe may touch

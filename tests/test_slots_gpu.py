@@ -47,6 +47,26 @@ def test_all_slots_together_equals_lockstep(op):
     assert torch.equal(outs, lock)
 
 
+@pytest.mark.parametrize("op", ["gdn", "kda"])
+def test_all_slots_together_equals_lockstep_at_serving_shape(op):
+    """B=128 H=32 d=128: the decode launches split the last 512 heads into
+    half-width tiles, in the per-slot kernel as in the lockstep ones, so the
+    two give the same bits there too (appends and folds, C=4)."""
+    T, Bsz, H, d, C = 9, 128, 32, 128, 4
+    x = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=37)
+    dev = gs.to_device(x, DEV)
+    lock, _, _ = gs.run_deltalog(dev, op, "bf16", C)
+    base = dev["S0"].clone()
+    st = dl.DeltaLogState(op, "bf16", base, C, slots=True)
+    for b in range(Bsz):
+        st.activate(b)
+    outs = torch.empty_like(lock)
+    for t in range(T):
+        st.step(out=outs[t], **_token(dev, t))
+    torch.cuda.synchronize()
+    assert torch.equal(outs, lock)
+
+
 def _segment_reference(x, op, slot, H, start, end, S0_seg, chk_end):
     """Oracle of one slot's heads over tokens [start, end) from S0_seg [H, d, d]."""
     sl = {}

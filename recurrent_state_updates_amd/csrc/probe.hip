@@ -48,8 +48,9 @@ __device__ __forceinline__ void probe_body(float *state, float *sink, int n, int
 }
 
 // One workgroup per head in the decode kernels' block order; at 128 x 128,
-// when the decode kernels split the launch's last heads into half-width
-// tiles (TAIL_HEADS_128, step_launch.h), the probe does the same.
+// where the decode kernels of 8-entry logs split the launch's last heads
+// into half-width tiles (TAIL_HEADS_128, step_launch.h), the probe does the
+// same (it follows those kernels, which serve every capacity up to 8).
 template <int DK, int DV, int NT, int KIND>
 __global__ __launch_bounds__(NT) void probe_kernel(float *state, float *sink, int N, int tail, float one) {
     const int nf = N - tail;

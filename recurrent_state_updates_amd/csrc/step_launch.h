@@ -7,20 +7,24 @@
 
 namespace dlk {
 
-// At 128 x 128 the decode modes run the launch's last TAIL_HEADS_128 heads
-// as two half-width tiles each (step_kernel_tail) when the launch has at
-// least four times as many heads (two or more rounds of workgroups on the
-// chip).  Measured on MI355X at B=128, H=32, C=8 (two alternating runs):
-// GDN 51.35-51.45 against 52.03-52.12 us/token back to back, KDA
-// 54.16-54.19 against 54.90-55.01, and the same with the cache refilled
-// before every launch; 256 tail heads did as well, 1024 half as well.  The
-// 64 x 64 heads keep whole heads: there the half tiles slowed RWKV6's folds.
+// At 128 x 128 the decode modes of the kernels built for 8-entry logs run
+// the launch's last TAIL_HEADS_128 heads as two half-width tiles each
+// (step_kernel_tail) when the launch has at least four times as many heads
+// (two or more rounds of workgroups on the chip).  Measured on MI355X at
+// B=128, H=32, C=8 (two alternating runs): GDN 51.35-51.45 against
+// 52.03-52.12 us/token back to back, KDA 54.16-54.19 against 54.90-55.01,
+// and the same with the cache refilled before every launch; 256 tail heads
+// did as well, 1024 half as well.  The kernels built for 16 and 32 entries
+// keep whole heads: with both tile forms in one kernel their folds need
+// 169-193 VGPRs, two waves per SIMD instead of four (a fold at C=32 took
+// 129 instead of 109 us).  The 64 x 64 heads keep whole heads too: there
+// the half tiles slowed RWKV6's folds.
 constexpr int TAIL_HEADS_128 = 512;
 
 template <int OP, typename TIn, int DK, int DV, int MODE, int CMAX>
 hipError_t launch_one(const StepParams &p, hipStream_t s) {
     constexpr int TV = Shape<DK, DV, MODE>::TV, NT = Shape<DK, DV, MODE>::NT;
-    if constexpr (DK == 128 && DV == 128 && TV == DV &&
+    if constexpr (DK == 128 && DV == 128 && TV == DV && CMAX == 8 &&
                   (MODE == MODE_APPEND || MODE == MODE_MERGE || MODE == MODE_AUTO)) {
         if (p.N >= 4 * TAIL_HEADS_128) {
             const unsigned blocks = (unsigned)(p.N + TAIL_HEADS_128);

@@ -2,7 +2,9 @@
 //
 // One workgroup owns a DK x TV tile of one head's fp32 state: all DK key rows
 // and TV of the DV value columns (the pages' value-tile parallelism; the
-// single-token kernels use TV = DV, one tile per head, see Shape).  Its
+// single-token kernels use TV = DV, one tile per head, see Shape, except for
+// the last heads of a 128 x 128 launch, which step_kernel_tail runs as two
+// half-width tiles each).  Its
 // threads stream the tile once from HBM with coalesced 16-byte loads (a tile
 // row is TV/4 lanes wide), keep it in registers, and do everything else
 // around that single pass:

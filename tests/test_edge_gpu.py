@@ -3,9 +3,11 @@
 The degenerate cases the method has: no decay (every log-decay stays 0), no
 update (beta = 0), an exact overwrite (beta = 1 on a basis key), zero keys,
 decays strong enough that the cumulative log-decay of a long cycle underflows
-exp2 in fp32, a single head, and an empty log (whose logical state is the
-base itself, bit for bit).
+exp2 in fp32, a single head, an empty log (whose logical state is the base
+itself, bit for bit), and a head count that splits unevenly over the launch
+shapes of the decode kernels.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -128,3 +130,29 @@ def test_empty_log_is_the_base_bit_for_bit(op):
     m = st.materialize()
     torch.cuda.synchronize()
     assert torch.equal(m, base)
+
+
+@pytest.mark.parametrize("op", ["gdn", "kda", "rwkv6"])
+def test_uneven_head_count_with_half_width_tail(op):
+    """2049 heads of 128 x 128 (B = 2049, H = 1) at C = 8: the decode launches
+    run the last 512 heads as two half-width tiles each, and the 1537 whole
+    heads before them do not divide evenly over the eight XCDs' block ranges.
+    A sample of heads that holds both sides of that boundary and both ends of
+    the batch, against the oracle: outputs at every step and states at steps
+    1, C - 1, C (right after the fold) and T."""
+    Bsz, H, d, C, T = 2049, 1, 128, 8, 12
+    N = Bsz * H
+    nf = N - 512  # heads decoded whole
+    x = workloads.generate(op, Bsz, H, d, d, T, "bf16", seed=316)
+    dev = gs.to_device(x, DEV)
+    rng = np.random.default_rng(7)
+    edges = [0, 1, nf - 2, nf - 1, nf, nf + 1, N - 2, N - 1]
+    heads = np.unique(np.concatenate([edges, rng.choice(N, 56, replace=False)]))
+    steps = [1, C - 1, C, T]
+    ref = gs.oracle_run(x, op, heads=heads, chk_steps=steps, nthreads=16)
+    outs, states, st = gs.run_deltalog(dev, op, "bf16", C, state_steps=steps, heads=heads)
+    hs = torch.as_tensor(heads, dtype=torch.long, device=outs.device)
+    gs.assert_outputs(outs.view(T, N, d)[:, hs].cpu().numpy(), ref["out"], (op, "uneven heads"))
+    for m, t in enumerate(steps):
+        gs.assert_state(states[t].numpy(), ref["states"][m], (op, "uneven heads", t))
+    assert st.log_length == T % C

@@ -868,7 +868,8 @@ def cold_cache_times(dl, d, w, Bsz, C, sh, traffic, dev, stream, outs, ntok=0, f
 
 
 def cpu_baseline(x, w, Bsz, tokens):
-    """The fp64 oracle on the host cores: all heads of the batch, the first ``tokens`` tokens."""
+    """The fp64 oracle on the host cores: all heads of the batch, the first ``tokens`` tokens.
+    A batch of fewer heads than threads also gets a one-thread figure (``one_thread``)."""
     import oracle
     try:
         ncpu = len(os.sched_getaffinity(0))
@@ -893,16 +894,32 @@ def cpu_baseline(x, w, Bsz, tokens):
     t0 = time.perf_counter()
     oracle.eager_run(w.op, q, k, v, beta, decay, bonus, S0, nthreads=threads)
     wall = time.perf_counter() - t0
+    one_thread = None
+    if N < threads:
+        # fewer heads than threads, where the pool cannot help: the one-thread
+        # figure too, repeated for at least 0.2 s of wall time
+        reps, t1 = 0, time.perf_counter()
+        while True:
+            oracle.eager_run(w.op, q, k, v, beta, decay, bonus, S0, nthreads=1)
+            reps += 1
+            el = time.perf_counter() - t1
+            if el >= 0.2:
+                break
+        one_thread = {"value": round(el * 1e6 / (reps * T), 2), "unit": "us/token", "cores": 1,
+                      "repeats": reps}
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
     except OSError:
         pass
-    return {"value": round(wall * 1e6 / T, 1), "unit": "us/token", "cores": threads, "kind": "oracle",
-            "sample": f"all {N} heads of {w.name} (B={Bsz}), first {T} tokens, fp64, "
-                      f"{threads} threads; wall {wall:.2f} s",
-            "cpu_model": model, "host_cpus_available": ncpu}
+    res = {"value": round(wall * 1e6 / T, 1), "unit": "us/token", "cores": threads, "kind": "oracle",
+           "sample": f"all {N} heads of {w.name} (B={Bsz}), first {T} tokens, fp64, "
+                     f"{threads} threads; wall {wall:.2f} s",
+           "cpu_model": model, "host_cpus_available": ncpu}
+    if one_thread is not None:
+        res["one_thread"] = one_thread
+    return res
 
 
 if __name__ == "__main__":

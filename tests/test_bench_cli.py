@@ -29,3 +29,20 @@ def test_help_lists_the_options():
     for opt in ("--steps", "--warmup", "--workload", "--C", "--cold", "--tokens", "--split-ablation",
                 "--staggered", "--calibrate-copy"):
         assert opt in r.stdout
+
+
+def test_cpu_baseline_of_the_small_workload_has_a_one_thread_figure():
+    """The oracle timing on the host: the small GDN workload (two heads) is
+    timed with the thread pool and with one thread; every field present."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+
+    w = workloads.WORKLOADS["gdn_b1_h2_d32"]
+    x = workloads.generate_workload(w)
+    res = bench.cpu_baseline(x, w, w.B, 16)
+    assert res["kind"] == "oracle" and res["unit"] == "us/token" and res["value"] > 0
+    assert res["cores"] >= 1 and "first 16 tokens" in res["sample"]
+    if res["cores"] > 2:
+        one = res["one_thread"]
+        assert one["cores"] == 1 and one["value"] > 0 and one["repeats"] >= 1
